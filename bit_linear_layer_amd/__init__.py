@@ -1,0 +1,239 @@
+"""NVFP4 W4A4 linear layers for MI355X (gfx950).
+
+A thin ctypes binding over ``libnvfp4.so`` (built from ``csrc/`` by
+``bit_linear_layer_amd.build``).  Each ``nvfp4_*`` function here has the name
+of the C entry point it calls and only marshals arguments: every step of the
+computation runs in the library's HIP kernels.  torch supplies device memory
+and the current stream.  There is no fallback: if the library is missing or
+a call fails, a ``NVFP4Error`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "NVFP4Error", "NVFP4Tensor", "load", "lib_path",
+    "nvfp4_quantize", "nvfp4_quantize_workspace_bytes", "nvfp4_gemm",
+    "nvfp4_gemm_fused_segments", "nvfp4_silu_mul", "nvfp4_status_string", "nvfp4_version",
+    "empty_nvfp4", "quantize", "gemm", "gemm_fused_segments", "silu_mul", "workspace_for",
+    "DTYPE_BF16", "DTYPE_F32", "SCALE_DYNAMIC", "SCALE_STATIC", "AMAX_PRECOMPUTED", "MAX_SEGMENTS",
+]
+
+DTYPE_BF16, DTYPE_F32 = 0, 1
+SCALE_DYNAMIC, SCALE_STATIC, AMAX_PRECOMPUTED = 0, 1, 2
+MAX_SEGMENTS = 16
+
+lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
+
+
+class NVFP4Error(RuntimeError):
+    pass
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ld_codes", ctypes.c_int64),
+                ("ld_scales", ctypes.c_int64)]
+
+
+class _Gate(ctypes.Structure):
+    _fields_ = [("b_segment", ctypes.c_int), ("a_segment", ctypes.c_int),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def load() -> ctypes.CDLL:
+    """Load libnvfp4.so (once).  Raises NVFP4Error if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise NVFP4Error(f"{lib_path} is missing: build it with "
+                             "`python -m bit_linear_layer_amd.build` (no fallback exists)")
+        lib = ctypes.CDLL(lib_path)
+        lib.nvfp4_quantize_workspace_bytes.argtypes = [_I64, _I64]
+        lib.nvfp4_quantize_workspace_bytes.restype = ctypes.c_size_t
+        lib.nvfp4_quantize.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P,
+                                       ctypes.c_int, _P, ctypes.c_size_t, _P]
+        lib.nvfp4_quantize.restype = ctypes.c_int
+        lib.nvfp4_gemm.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), _P,
+                                   ctypes.c_int, _I64, _P]
+        lib.nvfp4_gemm.restype = ctypes.c_int
+        lib.nvfp4_gemm_fused_segments.argtypes = [
+            ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.c_int,
+            ctypes.POINTER(ctypes.c_int64), _P, ctypes.POINTER(_Gate), _P, ctypes.c_int, _I64, _P]
+        lib.nvfp4_gemm_fused_segments.restype = ctypes.c_int
+        lib.nvfp4_silu_mul.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _P, ctypes.c_size_t, _P]
+        lib.nvfp4_silu_mul.restype = ctypes.c_int
+        lib.nvfp4_status_string.argtypes = [ctypes.c_int]
+        lib.nvfp4_status_string.restype = ctypes.c_char_p
+        lib.nvfp4_version.argtypes = []
+        lib.nvfp4_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def nvfp4_status_string(status: int) -> str:
+    return load().nvfp4_status_string(status).decode()
+
+
+def nvfp4_version() -> int:
+    return load().nvfp4_version()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise NVFP4Error(f"{what} failed: {nvfp4_status_string(status)} (status {status})")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream=None) -> int:
+    if stream is not None:
+        return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise NVFP4Error(f"unsupported dtype {t.dtype}")
+
+
+def _round_up(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+@dataclass
+class NVFP4Tensor:
+    """An NVFP4 matrix [rows, cols] in device memory: codes uint8
+    [rows, ld_codes] (two per byte, even element low), scales uint8
+    [rows, ld_scales] (E4M3 per 16 elements), global_scale float32 [1]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    global_scale: torch.Tensor
+    rows: int
+    cols: int
+
+    def descriptor(self) -> _Tensor:
+        return _Tensor(self.codes.data_ptr(), self.scales.data_ptr(), self.global_scale.data_ptr(),
+                       self.rows, self.cols, self.codes.stride(0), self.scales.stride(0))
+
+    def row_slice(self, r0: int, r1: int) -> "NVFP4Tensor":
+        return NVFP4Tensor(self.codes[r0:r1], self.scales[r0:r1], self.global_scale, r1 - r0, self.cols)
+
+
+def empty_nvfp4(rows: int, cols: int, device="cuda") -> NVFP4Tensor:
+    """Allocate an NVFP4 matrix with the row strides the kernels require
+    (codes rows on 16-byte, scale rows on 8-byte boundaries)."""
+    ldc = _round_up(max(cols // 2, 1), 16)
+    lds = _round_up(max(cols // 16, 1), 8)
+    codes = torch.empty((rows, ldc), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, lds), dtype=torch.uint8, device=device)
+    g = torch.empty(1, dtype=torch.float32, device=device)
+    return NVFP4Tensor(codes, scales, g, rows, cols)
+
+
+def nvfp4_quantize_workspace_bytes(rows: int, cols: int) -> int:
+    return int(load().nvfp4_quantize_workspace_bytes(rows, cols))
+
+
+def workspace_for(rows: int, cols: int, device="cuda") -> torch.Tensor:
+    return torch.empty(nvfp4_quantize_workspace_bytes(rows, cols) // 4, dtype=torch.float32, device=device)
+
+
+def nvfp4_quantize(x: torch.Tensor, q: NVFP4Tensor, flags: int = SCALE_DYNAMIC,
+                   workspace: torch.Tensor | None = None, stream=None) -> None:
+    """C ``nvfp4_quantize`` on a 2-D bf16/float32 tensor x (rows may be
+    strided) into the preallocated ``q``."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise NVFP4Error("x must be a 2-D tensor with contiguous rows")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().nvfp4_quantize(
+        x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
+        q.codes.data_ptr(), q.codes.stride(0), q.scales.data_ptr(), q.scales.stride(0),
+        q.global_scale.data_ptr(), flags, _ptr(workspace), ws_bytes, _stream(x.device, stream))
+    _check(st, "nvfp4_quantize")
+
+
+def nvfp4_gemm(a: NVFP4Tensor, w: NVFP4Tensor, out: torch.Tensor, stream=None) -> None:
+    """C ``nvfp4_gemm``: out[M, N] = A W^T with both global scales."""
+    da, dw = a.descriptor(), w.descriptor()
+    st = load().nvfp4_gemm(ctypes.byref(da), ctypes.byref(dw), out.data_ptr(), _dtype_code(out),
+                           out.stride(0), _stream(out.device, stream))
+    _check(st, "nvfp4_gemm")
+
+
+def nvfp4_gemm_fused_segments(a: NVFP4Tensor, w: NVFP4Tensor, seg_offsets, seg_global_scales: torch.Tensor,
+                              out: torch.Tensor, gate: dict | None = None, stream=None) -> None:
+    """C ``nvfp4_gemm_fused_segments``.  seg_offsets: host ints [n+1];
+    seg_global_scales: device float32 [n]; gate: None or dict(b_segment,
+    a_segment, A_log, dt_bias) with device float32 tensors."""
+    offs = (ctypes.c_int64 * len(seg_offsets))(*[int(o) for o in seg_offsets])
+    g = None
+    if gate is not None:
+        g = _Gate(int(gate.get("b_segment", -1)), int(gate.get("a_segment", -1)),
+                  _ptr(gate.get("A_log")), _ptr(gate.get("dt_bias")))
+    da, dw = a.descriptor(), w.descriptor()
+    st = load().nvfp4_gemm_fused_segments(
+        ctypes.byref(da), ctypes.byref(dw), len(seg_offsets) - 1, offs, seg_global_scales.data_ptr(),
+        None if g is None else ctypes.byref(g), out.data_ptr(), _dtype_code(out), out.stride(0),
+        _stream(out.device, stream))
+    _check(st, "nvfp4_gemm_fused_segments")
+
+
+def nvfp4_silu_mul(gu: torch.Tensor, h: torch.Tensor, inter: int, amax_workspace: torch.Tensor | None = None,
+                   stream=None) -> None:
+    """C ``nvfp4_silu_mul``: h = bf16(silu(gu[:, :inter]) * gu[:, inter:2*inter])."""
+    ws_bytes = 0 if amax_workspace is None else amax_workspace.numel() * amax_workspace.element_size()
+    st = load().nvfp4_silu_mul(gu.data_ptr(), gu.shape[0], inter, gu.stride(0), h.data_ptr(), h.stride(0),
+                               _ptr(amax_workspace), ws_bytes, _stream(gu.device, stream))
+    _check(st, "nvfp4_silu_mul")
+
+
+# ----------------------------------------------------------- conveniences
+
+def quantize(x: torch.Tensor, static_scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+             out: NVFP4Tensor | None = None, amax_precomputed: bool = False) -> NVFP4Tensor:
+    """Allocate (unless ``out``) and quantize x; dynamic global scale unless
+    ``static_scale`` (device float32 [1]) is given."""
+    q = out if out is not None else empty_nvfp4(x.shape[0], x.shape[1], x.device)
+    if static_scale is not None:
+        q.global_scale.copy_(static_scale)
+        nvfp4_quantize(x, q, SCALE_STATIC, None)
+    else:
+        ws = workspace if workspace is not None else workspace_for(x.shape[0], x.shape[1], x.device)
+        nvfp4_quantize(x, q, AMAX_PRECOMPUTED if amax_precomputed else SCALE_DYNAMIC, ws)
+    return q
+
+
+def gemm(a: NVFP4Tensor, w: NVFP4Tensor, out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    o = out if out is not None else torch.empty((a.rows, w.rows), dtype=out_dtype, device=a.codes.device)
+    nvfp4_gemm(a, w, o)
+    return o
+
+
+def gemm_fused_segments(a: NVFP4Tensor, w: NVFP4Tensor, seg_offsets, seg_global_scales: torch.Tensor,
+                        gate: dict | None = None, out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    o = out if out is not None else torch.empty((a.rows, w.rows), dtype=out_dtype, device=a.codes.device)
+    nvfp4_gemm_fused_segments(a, w, seg_offsets, seg_global_scales, o, gate)
+    return o
+
+
+def silu_mul(gu: torch.Tensor, amax_workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    inter = gu.shape[1] // 2
+    h = out if out is not None else torch.empty((gu.shape[0], inter), dtype=torch.bfloat16, device=gu.device)
+    nvfp4_silu_mul(gu, h, inter, amax_workspace)
+    return h

@@ -1,0 +1,186 @@
+// C ABI of the NVFP4 W4A4 library: argument validation (before any HIP
+// call) and dispatch to the kernels' launchers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "internal.h"
+#include "nvfp4.h"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // kernels index rows/cols with int
+
+thread_local char g_hip_msg[256] = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return NVFP4_OK;
+  snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+  return NVFP4_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_tensor(const nvfp4_tensor* t) {
+  if (t == nullptr || t->codes == nullptr || t->scales == nullptr) return NVFP4_ERR_NULL;
+  if (t->rows <= 0 || t->cols <= 0 || t->cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (t->rows >= kIndexLimit || t->cols >= kIndexLimit) return NVFP4_ERR_RANGE;
+  if (t->ld_codes < t->cols / 2 || t->ld_codes % 16 != 0) return NVFP4_ERR_STRIDE;
+  if (t->ld_scales < t->cols / 16 || t->ld_scales % 8 != 0) return NVFP4_ERR_STRIDE;
+  if (!aligned(t->codes, 16) || !aligned(t->scales, 8)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+int check_out(const void* out, int out_dtype, int64_t ld_out, int64_t n) {
+  if (out == nullptr) return NVFP4_ERR_NULL;
+  if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (ld_out < n) return NVFP4_ERR_STRIDE;
+  if (!aligned(out, out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols < 16) return sizeof(float);
+  return sizeof(float) * (size_t)partial_count(rows, cols, 16);
+}
+
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                   float* global_scale, int flags, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (x == nullptr || codes == nullptr || scales == nullptr || global_scale == nullptr)
+    return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (flags != NVFP4_SCALE_DYNAMIC && flags != NVFP4_SCALE_STATIC && flags != NVFP4_AMAX_PRECOMPUTED)
+    return NVFP4_ERR_FLAGS;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows >= kIndexLimit || cols >= kIndexLimit) return NVFP4_ERR_RANGE;
+  const int esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (ld_x < cols || (ld_x * esz) % 16 != 0) return NVFP4_ERR_STRIDE;
+  if (ld_codes < cols / 2 || ld_codes % 8 != 0) return NVFP4_ERR_STRIDE;
+  if (ld_scales < cols / 16) return NVFP4_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(global_scale, 4)) return NVFP4_ERR_ALIGN;
+  const bool dynamic = flags != NVFP4_SCALE_STATIC;
+  const int np = partial_count(rows, cols, 16);
+  if (dynamic) {
+    if (workspace == nullptr) return NVFP4_ERR_WORKSPACE;
+    if (workspace_bytes < sizeof(float) * (size_t)np) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return NVFP4_ERR_ALIGN;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  float* partials = (float*)workspace;
+  if (flags == NVFP4_SCALE_DYNAMIC) {
+    const int st = hip_status(launch_amax(x, x_dtype, rows, cols, ld_x, partials, np, s));
+    if (st != NVFP4_OK) return st;
+  }
+  return hip_status(launch_quantize(x, x_dtype, rows, cols, ld_x, codes, ld_codes, scales,
+                                    ld_scales, global_scale, dynamic ? 0 : 1, partials, np, s));
+}
+
+int nvfp4_gemm_fused_segments(const nvfp4_tensor* a, const nvfp4_tensor* w, int n_segments,
+                              const int64_t* seg_offsets, const float* seg_global_scales,
+                              const nvfp4_gdn_gate* gate, void* out, int out_dtype, int64_t ld_out,
+                              void* stream) {
+  int st = check_tensor(a);
+  if (st != NVFP4_OK) return st;
+  st = check_tensor(w);
+  if (st != NVFP4_OK) return st;
+  if (a->global_scale == nullptr) return NVFP4_ERR_NULL;
+  if (a->cols != w->cols) return NVFP4_ERR_SHAPE;
+  st = check_out(out, out_dtype, ld_out, w->rows);
+  if (st != NVFP4_OK) return st;
+  if (n_segments < 1 || n_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_SEGMENTS;
+  if (seg_offsets == nullptr || seg_global_scales == nullptr) return NVFP4_ERR_NULL;
+  if (seg_offsets[0] != 0 || seg_offsets[n_segments] != w->rows) return NVFP4_ERR_SEGMENTS;
+  for (int s = 0; s < n_segments; ++s)
+    if (seg_offsets[s + 1] <= seg_offsets[s]) return NVFP4_ERR_SEGMENTS;
+
+  GemmArgs p{};
+  p.a_codes = a->codes;
+  p.a_scales = a->scales;
+  p.lda_c = a->ld_codes;
+  p.lda_s = a->ld_scales;
+  p.w_codes = w->codes;
+  p.w_scales = w->scales;
+  p.ldw_c = w->ld_codes;
+  p.ldw_s = w->ld_scales;
+  p.out = out;
+  p.ld_out = ld_out;
+  p.out_bf16 = out_dtype == NVFP4_DTYPE_BF16;
+  p.M = (int)a->rows;
+  p.N = (int)w->rows;
+  p.K = (int)a->cols;
+  p.ep.n_seg = n_segments;
+  for (int s = 0; s <= n_segments; ++s) p.ep.seg_off[s] = (int)seg_offsets[s];
+  p.ep.seg_g = seg_global_scales;
+  p.ep.a_g = a->global_scale;
+  p.ep.b_seg = -1;
+  p.ep.a_seg = -1;
+  if (gate != nullptr) {
+    const int bs = gate->b_segment, as = gate->a_segment;
+    if (bs < -1 || bs >= n_segments || as < -1 || as >= n_segments) return NVFP4_ERR_GATE;
+    if (bs >= 0 && bs == as) return NVFP4_ERR_GATE;
+    if (as >= 0 && (gate->A_log == nullptr || gate->dt_bias == nullptr)) return NVFP4_ERR_GATE;
+    p.ep.b_seg = bs;
+    p.ep.a_seg = as;
+    p.ep.A_log = gate->A_log;
+    p.ep.dt_bias = gate->dt_bias;
+  }
+  return hip_status(launch_gemm(p, (hipStream_t)stream));
+}
+
+int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* w, void* out, int out_dtype,
+               int64_t ld_out, void* stream) {
+  int st = check_tensor(w);
+  if (st != NVFP4_OK) return st;
+  if (w->global_scale == nullptr) return NVFP4_ERR_NULL;
+  const int64_t offs[2] = {0, w->rows};
+  return nvfp4_gemm_fused_segments(a, w, 1, offs, w->global_scale, nullptr, out, out_dtype,
+                                   ld_out, stream);
+}
+
+int nvfp4_silu_mul(const void* gu, int64_t rows, int64_t inter, int64_t ld_gu, void* h,
+                   int64_t ld_h, void* amax_workspace, size_t workspace_bytes, void* stream) {
+  if (gu == nullptr || h == nullptr) return NVFP4_ERR_NULL;
+  if (rows <= 0 || inter <= 0 || inter % 8 != 0) return NVFP4_ERR_SHAPE;
+  if (rows >= kIndexLimit || inter >= kIndexLimit) return NVFP4_ERR_RANGE;
+  if (ld_gu < 2 * inter || ld_gu % 8 != 0 || ld_h < inter || ld_h % 8 != 0) return NVFP4_ERR_STRIDE;
+  if (!aligned(gu, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
+  // Same partial count as a quantize of h (which needs inter % 16 == 0).
+  const int np = partial_count(rows, inter, 16);
+  if (amax_workspace != nullptr) {
+    if (inter % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (workspace_bytes < sizeof(float) * (size_t)np) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(amax_workspace, 4)) return NVFP4_ERR_ALIGN;
+  }
+  return hip_status(launch_silu_mul((const uint16_t*)gu, rows, inter, ld_gu, (uint16_t*)h, ld_h,
+                                    (float*)amax_workspace, np, (hipStream_t)stream));
+}
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "bad shape (rows/cols must be > 0, cols % 16 == 0, K must match)";
+    case NVFP4_ERR_DTYPE: return "unknown dtype code";
+    case NVFP4_ERR_STRIDE: return "leading dimension too small or not a multiple of the required alignment";
+    case NVFP4_ERR_ALIGN: return "base pointer misaligned";
+    case NVFP4_ERR_SEGMENTS: return "bad segment table";
+    case NVFP4_ERR_GATE: return "bad gate specification";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_FLAGS: return "unknown flags";
+    case NVFP4_ERR_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+    case NVFP4_ERR_RANGE: return "size beyond 2^31";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_version(void) { return 100; }
+
+}  // extern "C"

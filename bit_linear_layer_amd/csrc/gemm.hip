@@ -1,0 +1,363 @@
+// W4A4 NVFP4 GEMM for gfx950:  out[m, n] = g_a * g_w[seg(n)] * sum_k A[m,k] * W[n,k]
+// with A and W given as E2M1 codes + one E4M3 scale per 16 elements
+// (evolve.pub review of arXiv 2609.04098, "Scope & Claims"), the weight made
+// of row segments that each keep their own global scale (the fused-GEMM
+// global-scale mismatch, chatpaper.ai English abstract; evolve.pub review,
+// "Key claims under review"), and an optional GDN gate epilogue
+// (chatpaper.ai abstract, mechanism (ii)).
+//
+// Why fp16 MFMA on decoded operands.  gfx950's scaled MFMAs take one E8M0
+// (power-of-two) scale per 32 elements; an E4M3 scale per 16 elements fits
+// neither the block size nor the scale format, and folding it into the
+// element needs 6 significand bits, which FP8/FP6/FP4 lack.  But
+// e2m1 * e4m3 has <= 6 significant bits and lies in [2^-10, 2688], so it is
+// EXACT in fp16 (11 bits, normal range 2^-14..65504).  Products of two such
+// values have <= 12 bits and are exact in fp32; only the fp32 accumulation
+// rounds.  The global scales are applied once, in the epilogue.
+//
+// Data path per workgroup (BM x BN output tile, BK = 128):
+//   global -> registers -> LDS, raw packed codes + scale bytes (0.5625 B per
+//   element, 3.6x less LDS traffic than staging fp16), double-buffered;
+//   each wave reads its fragments from LDS in MFMA lane order (one 16-byte
+//   read per lane, consecutive lanes consecutive addresses) and decodes them
+//   in registers: 4 x v_cvt_scalef32_pk_f16_fp4 + 4 x v_pk_mul_f16 per
+//   8 elements; then v_mfma_f32_32x32x16_f16.
+//
+// K order inside a 128-wide K tile.  The MFMA sums over its 16 k values, so
+// any permutation of k that A and W share is allowed.  Lane (row, h) of a
+// fragment feeds the k-values {64h + 8t + e : e < 8} at k-step t (t < 8),
+// so one lane's codes for a whole tile are 32 contiguous bytes of its row,
+// and its scales are 4 contiguous bytes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBK = 128;              // K elements per tile
+constexpr int kRowCodeBytes = kBK / 2;  // 64 code bytes per row per tile
+constexpr int kRowScaleBytes = kBK / 16;  // 8 scale bytes per row per tile
+
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int kThreads = WGM * WGN * 64;
+  static constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 fragments per wave
+  static constexpr int kACode = BM * kRowCodeBytes;
+  static constexpr int kBCode = BN * kRowCodeBytes;
+  static constexpr int kAScale = BM * kRowScaleBytes;
+  static constexpr int kBScale = BN * kRowScaleBytes;
+  static constexpr int kStage = kACode + kBCode + kAScale + kBScale;
+  static constexpr int kChunks = (BM + BN) * 4;  // 16-byte code chunks per stage
+  static constexpr int kChunkIters = (kChunks + kThreads - 1) / kThreads;
+  static constexpr int kScaleIters = (BM + BN + kThreads - 1) / kThreads;
+  static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
+};
+
+// LDS byte offset of 16-byte chunk q (0..3) of tile row `row`: fragment
+// (row / 32) holds 2 KB = [chunk parity c][lane][16 B], lane = 32*(q/2) + row%32.
+__device__ inline int code_slot(int row, int q) {
+  return (row >> 5) * 2048 + (q & 1) * 1024 + ((((q >> 1) << 5) | (row & 31)) << 4);
+}
+// LDS byte offset of scale dword h (0..1) of tile row `row`: [fragment][lane][4 B].
+__device__ inline int scale_slot(int row, int h) {
+  return (row >> 5) * 256 + ((((h) << 5) | (row & 31)) << 2);
+}
+
+// E4M3 byte -> fp16 pair (s, s), exact: the byte shifted into an fp16's
+// exponent/mantissa fields is s * 2^-8 (normal and subnormal alike).
+__device__ inline half2v scale_pair(uint32_t sdw, int idx) {
+  const uint32_t b = (sdw >> (8 * idx)) & 0xFFu;
+  const uint32_t bits = (b << 7) | (b << 23);
+  half2v h = __builtin_bit_cast(half2v, bits);
+  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  return h * k256;
+}
+
+// 8 E2M1 codes (one dword) times their block scale -> 8 exact fp16 values.
+__device__ inline half8 decode8(uint32_t codes, half2v s2) {
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+  p0 *= s2;
+  p1 *= s2;
+  p2 *= s2;
+  p3 *= s2;
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline float sigmoidf_(float x) {
+  const float e = expf(-fabsf(x));
+  return x >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+}
+__device__ inline float softplusf_(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
+
+// Stage one K tile of A and W into registers.
+template <class C>
+struct TileLoader {
+  u32x4 chunk[C::kChunkIters];
+  uint2 sc[C::kScaleIters];
+
+  __device__ void load(const GemmArgs& p, int m0, int n0, int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int it = 0; it < C::kChunkIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (id < C::kChunks) {
+        const bool isB = id >= C::BM * 4;
+        const int lid = isB ? id - C::BM * 4 : id;
+        const int row = lid >> 2, q = lid & 3;
+        const int grow = isB ? min(n0 + row, p.N - 1) : min(m0 + row, p.M - 1);
+        const uint8_t* base = isB ? p.w_codes + (int64_t)grow * p.ldw_c : p.a_codes + (int64_t)grow * p.lda_c;
+        const int kk = k0 + q * 32;  // first element of the chunk
+        const int rem = p.K - kk;
+        const uint8_t* src = base + (kk >> 1);
+        if (rem >= 32) {
+          v = *reinterpret_cast<const u32x4*>(src);
+        } else if (rem > 0) {  // rem == 16: the first 8 bytes only
+          const uint2 h = *reinterpret_cast<const uint2*>(src);
+          v[0] = h.x;
+          v[1] = h.y;
+        }
+      }
+      chunk[it] = v;
+    }
+#pragma unroll
+    for (int it = 0; it < C::kScaleIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
+      uint2 v = make_uint2(0u, 0u);
+      if (id < C::BM + C::BN) {
+        const bool isB = id >= C::BM;
+        const int row = isB ? id - C::BM : id;
+        const int grow = isB ? min(n0 + row, p.N - 1) : min(m0 + row, p.M - 1);
+        const uint8_t* src = (isB ? p.w_scales + (int64_t)grow * p.ldw_s : p.a_scales + (int64_t)grow * p.lda_s) + kt * kRowScaleBytes;
+        const int nb = (p.K >> 4) - kt * kRowScaleBytes;  // valid scale bytes from here
+        if (nb >= 8) {
+          v = *reinterpret_cast<const uint2*>(src);
+        } else {
+          uint32_t lo = 0, hi = 0;
+          for (int b = 0; b < nb; ++b) {
+            const uint32_t byte = src[b];
+            if (b < 4) lo |= byte << (8 * b);
+            else hi |= byte << (8 * (b - 4));
+          }
+          v = make_uint2(lo, hi);
+        }
+      }
+      sc[it] = v;
+    }
+  }
+
+  __device__ void store(uint8_t* stage) const {
+#pragma unroll
+    for (int it = 0; it < C::kChunkIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
+      if (id < C::kChunks) {
+        const bool isB = id >= C::BM * 4;
+        const int lid = isB ? id - C::BM * 4 : id;
+        uint8_t* dst = stage + (isB ? C::kACode : 0) + code_slot(lid >> 2, lid & 3);
+        *reinterpret_cast<u32x4*>(dst) = chunk[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < C::kScaleIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
+      if (id < C::BM + C::BN) {
+        const bool isB = id >= C::BM;
+        const int row = isB ? id - C::BM : id;
+        uint8_t* reg = stage + C::kACode + C::kBCode + (isB ? C::kAScale : 0);
+        *reinterpret_cast<uint32_t*>(reg + scale_slot(row, 0)) = sc[it].x;
+        *reinterpret_cast<uint32_t*>(reg + scale_slot(row, 1)) = sc[it].y;
+      }
+    }
+  }
+};
+
+// Map the linear workgroup id to an output tile.  Workgroups are dealt to
+// the 8 XCDs round-robin; renumber them so each XCD works on a contiguous
+// range of tiles (sharing its L2), then walk that range in column-major
+// groups of kGroupM tile rows so neighbours share A and W panels.
+__device__ inline void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcd = 8, kGroupM = 8;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  const int x = bid % kXcd, slot = bid / kXcd;
+  const int l = x * q + min(x, r) + slot;
+  const int group_size = kGroupM * tiles_n;
+  const int group = l / group_size;
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in = l - group * group_size;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(const GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tiles_m = (p.M + C::BM - 1) / C::BM;
+  const int tiles_n = (p.N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_of((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int fm0 = wm * C::FM, fn0 = wn * C::FN;  // first fragment (of 32 rows/cols) in the tile
+
+  floatx16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (p.K + kBK - 1) / kBK;
+  TileLoader<C> ld;
+  ld.load(p, m0, n0, 0);
+  ld.store(smem);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) ld.load(p, m0, n0, kt + 1);
+    const uint8_t* st = smem + (kt & 1) * C::kStage;
+    const uint8_t* sA = st;
+    const uint8_t* sB = st + C::kACode;
+    const uint8_t* sAs = st + C::kACode + C::kBCode;
+    const uint8_t* sBs = sAs + C::kAScale;
+
+    u32x4 ac[C::FM][2], bc[C::FN][2];
+    uint32_t as[C::FM], bs[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      ac[i][0] = *reinterpret_cast<const u32x4*>(sA + (fm0 + i) * 2048 + lane * 16);
+      ac[i][1] = *reinterpret_cast<const u32x4*>(sA + (fm0 + i) * 2048 + 1024 + lane * 16);
+      as[i] = *reinterpret_cast<const uint32_t*>(sAs + (fm0 + i) * 256 + lane * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      bc[j][0] = *reinterpret_cast<const u32x4*>(sB + (fn0 + j) * 2048 + lane * 16);
+      bc[j][1] = *reinterpret_cast<const u32x4*>(sB + (fn0 + j) * 2048 + 1024 + lane * 16);
+      bs[j] = *reinterpret_cast<const uint32_t*>(sBs + (fn0 + j) * 256 + lane * 4);
+    }
+
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {  // pairs of k-steps share one scale byte
+      half2v sa2[C::FM], sb2[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) sa2[i] = scale_pair(as[i], t2);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) sb2[j] = scale_pair(bs[j], t2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = 2 * t2 + u;
+        half8 a[C::FM], b[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) a[i] = decode8(ac[i][t >> 2][t & 3], sa2[i]);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) b[j] = decode8(bc[j][t >> 2][t & 3], sb2[j]);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+
+    if (kt + 1 < nk) ld.store(smem + ((kt + 1) & 1) * C::kStage);
+    __syncthreads();
+  }
+
+  // Epilogue: per output column its segment's global scale, then the gates.
+  const float ga = *p.ep.a_g;
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const int n = n0 + (fn0 + j) * 32 + (lane & 31);
+    if (n >= p.N) continue;
+    int seg = 0;
+    for (int s = 1; s < p.ep.n_seg; ++s) seg += (n >= p.ep.seg_off[s]) ? 1 : 0;
+    const float sc = ga * p.ep.seg_g[seg];
+    const int kind = seg == p.ep.b_seg ? 1 : (seg == p.ep.a_seg ? 2 : 0);
+    float alog = 0.0f, dtb = 0.0f;
+    if (kind == 2) {
+      const int h = n - p.ep.seg_off[seg];
+      alog = expf(p.ep.A_log[h]);
+      dtb = p.ep.dt_bias[h];
+    }
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int mb = m0 + (fm0 + i) * 32 + 4 * (lane >> 5);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (m >= p.M) continue;
+        float v = acc[i][j][r] * sc;
+        if (kind == 1) v = sigmoidf_(v);
+        else if (kind == 2) v = -alog * softplusf_(v + dtb);
+        if (p.out_bf16)
+          reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.ld_out + n] = (uint16_t)f32_to_bf16_bits(v);
+        else
+          reinterpret_cast<float*>(p.out)[(int64_t)m * p.ld_out + n] = v;
+      }
+    }
+  }
+}
+
+template <class C>
+hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
+  const int tiles_m = (p.M + C::BM - 1) / C::BM;
+  const int tiles_n = (p.N + C::BN - 1) / C::BN;
+  const int64_t nblocks = (int64_t)tiles_m * tiles_n;
+  const size_t lds = 2 * (size_t)C::kStage;
+  static bool attr_done = false;  // raising the dynamic-LDS limit is idempotent
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  gemm_kernel<C><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p);
+  return hipGetLastError();
+}
+
+using CfgL = TileCfg<256, 256, 2, 2>;  // large prefill shapes
+using CfgM = TileCfg<128, 128, 2, 2>;  // medium shapes / better wave fill
+using CfgS = TileCfg<32, 128, 1, 4>;   // M <= 32
+
+double fill(int64_t tiles) {
+  const int64_t waves = (tiles + 255) / 256;
+  return (double)tiles / (double)(waves * 256);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {
+  if (p.M <= 32) return launch_cfg<CfgS>(p, s);
+  const int64_t tl = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
+  if (p.M >= 256 && p.N >= 256 && fill(tl) >= 0.8 * fill(tmd)) return launch_cfg<CfgL>(p, s);
+  return launch_cfg<CfgM>(p, s);
+}
+
+}  // namespace nvfp4

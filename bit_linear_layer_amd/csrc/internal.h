@@ -1,0 +1,59 @@
+// Internal declarations shared by the kernels' launchers and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+
+namespace nvfp4 {
+
+// Amax partials: one float per workgroup of the amax pass (or of the fused
+// SiLU*mul kernel), reduced again by every workgroup of the quantize pass.
+constexpr int kMaxPartials = 1024;
+constexpr int kElemThreads = 256;  // workgroup size of the elementwise kernels
+
+// Number of amax partials (= workgroups) used for a [rows, cols] tensor
+// walked in chunks of `chunk` elements per thread.
+int partial_count(int64_t rows, int64_t cols, int chunk);
+
+hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                       float* partials, int n_partials, hipStream_t s);
+
+// mode: 0 = dynamic (reduce partials, write *g), 1 = static (read *g).
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                           float* g, int mode, const float* partials, int n_partials,
+                           hipStream_t s);
+
+hipError_t launch_silu_mul(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
+                           uint16_t* h, int64_t ld_h, float* partials, int n_partials,
+                           hipStream_t s);
+
+struct EpilogueArgs {
+  int n_seg;
+  int seg_off[NVFP4_MAX_SEGMENTS + 1];  // output-column offsets of the segments
+  const float* seg_g;                   // device [n_seg] weight global scales
+  const float* a_g;                     // device activation global scale
+  int b_seg, a_seg;                     // gate segments, -1 = none
+  const float* A_log;
+  const float* dt_bias;
+};
+
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  int64_t lda_c, lda_s;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  int64_t ldw_c, ldw_s;
+  void* out;
+  int64_t ld_out;
+  int out_bf16;
+  int M, N, K;
+  EpilogueArgs ep;
+};
+
+hipError_t launch_gemm(const GemmArgs& args, hipStream_t s);
+
+}  // namespace nvfp4

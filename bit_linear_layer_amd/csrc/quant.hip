@@ -1,0 +1,229 @@
+// NVFP4 quantization kernels for gfx950: the amax pass and the quantize pass.
+//
+// Format (evolve.pub review of arXiv 2609.04098, "Scope & Claims";
+// thevalue.engineering article, section on the fragility myth): E2M1 codes
+// with one E4M3 scale per 16 consecutive elements, plus one float32 global
+// scale per tensor.  The activations of every linear layer go through this
+// on the fly (chatpaper.ai English abstract: W4A4 on all linear layers).
+//
+// Exact rounding without division per element.  For a block with E4M3 scale
+// s and global scale g, the magnitude code of x is the number of E2M1
+// midpoints mu in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5} that |x| passes,
+// where "passes" is > for the midpoints whose tie goes down (to an even
+// code) and >= for those whose tie goes up.  |x| has <= 24 significant bits,
+// mu * s * g <= 3 + 4 + 24 = 31 bits, so both are exact float64 numbers and
+// the float64 comparisons are the exact-real decisions.  The block scale is
+// one correctly rounded float64 division amax_b / (6 g): a non-tie quotient
+// lies >= 2^-31 (relative) from every E4M3 midpoint, far above float64's
+// 2^-53 rounding, so rounding the float64 quotient to E4M3 is exact.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Max over the workgroup (kElemThreads threads); every thread gets it.
+__device__ inline float block_max(float v) {
+  __shared__ float red[kElemThreads / 64];
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kElemThreads / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Load one 16-element block starting at p (16-byte aligned) as floats.
+template <int DT>
+__device__ inline void load_block16(const uint8_t* p, float v[16]) {
+  if constexpr (DT == NVFP4_DTYPE_BF16) {
+    const uint4 q0 = *reinterpret_cast<const uint4*>(p);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16);
+    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 q = *reinterpret_cast<const float4*>(p + 16 * i);
+      v[4 * i] = q.x;
+      v[4 * i + 1] = q.y;
+      v[4 * i + 2] = q.z;
+      v[4 * i + 3] = q.w;
+    }
+  }
+}
+
+// Walks the 16-element blocks of a [rows, bpr*16] matrix with a grid-stride
+// loop, keeping (row, block-in-row) without a division per step.
+struct BlockWalk {
+  int64_t r, j, bpr, rows;
+  int64_t dr, dj;
+  __device__ BlockWalk(int64_t rows_, int64_t bpr_) : rows(rows_), bpr(bpr_) {
+    const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    r = start / bpr;
+    j = start - r * bpr;
+    dr = stride / bpr;
+    dj = stride - dr * bpr;
+  }
+  __device__ bool valid() const { return r < rows; }
+  __device__ void next() {
+    r += dr;
+    j += dj;
+    if (j >= bpr) {
+      j -= bpr;
+      ++r;
+    }
+  }
+};
+
+template <int DT>
+__global__ __launch_bounds__(kElemThreads) void amax_kernel(const uint8_t* __restrict__ x,
+                                                            int64_t ld_bytes, int64_t rows,
+                                                            int64_t bpr,
+                                                            float* __restrict__ partials) {
+  constexpr int kBlockBytes = DT == NVFP4_DTYPE_BF16 ? 32 : 64;
+  float m = 0.0f;
+  for (BlockWalk it(rows, bpr); it.valid(); it.next()) {
+    float v[16];
+    load_block16<DT>(x + it.r * ld_bytes + it.j * kBlockBytes, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// E4M3 (OCP FN) code nearest to r >= 0: ties to even code, r >= 448 -> 0x7E.
+__device__ inline uint32_t e4m3_rne(double r) {
+  if (r >= 448.0) return 0x7Eu;
+  if (r < 0x1p-6) return (uint32_t)rint(r * 512.0);  // subnormal grid k * 2^-9 (8 = min normal)
+  int e;
+  const double f = frexp(r, &e);                     // r = f * 2^e, f in [0.5, 1)
+  const uint32_t q = (uint32_t)rint(f * 16.0);       // 8..16, 16 carries into the exponent
+  const uint32_t code = (uint32_t)((e + 6) << 3) + q - 8u;
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ inline double e4m3_value(uint32_t code) {
+  const uint32_t e = code >> 3, m = code & 7u;
+  return e == 0 ? (double)m * 0x1p-9 : ldexp(1.0 + (double)m * 0.125, (int)e - 7);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kElemThreads) void quantize_kernel(
+    const uint8_t* __restrict__ x, int64_t ld_bytes, int64_t rows, int64_t bpr,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
+    int64_t ld_scales, float* __restrict__ gptr, int mode, const float* __restrict__ partials,
+    int n_partials) {
+  constexpr int kBlockBytes = DT == NVFP4_DTYPE_BF16 ? 32 : 64;
+  float g;
+  if (mode == 0) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n_partials; i += blockDim.x) m = fmaxf(m, partials[i]);
+    m = block_max(m);
+    g = (float)((double)m / 2688.0);  // one correctly rounded division (53 >= 2*24+2)
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gptr = g;
+  } else {
+    g = *gptr;
+  }
+  const double g64 = (double)g;
+  const double g6 = 6.0 * g64;  // exact
+
+  for (BlockWalk it(rows, bpr); it.valid(); it.next()) {
+    float v[16];
+    load_block16<DT>(x + it.r * ld_bytes + it.j * kBlockBytes, v);
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
+
+    uint32_t s = 0;
+    if (g != 0.0f && amax_b != 0.0f) s = e4m3_rne((double)amax_b / g6);
+
+    // thresholds mu * s * g, exact in float64; s == 0 -> every magnitude code is 0
+    double t0, t1, t2, t3, t4, t5, t6;
+    if (s == 0) {
+      t0 = t1 = t2 = t3 = t4 = t5 = t6 = __builtin_inf();
+    } else {
+      const double sg = e4m3_value(s) * g64;
+      t0 = 0.25 * sg; t1 = 0.75 * sg; t2 = 1.25 * sg; t3 = 1.75 * sg;
+      t4 = 2.5 * sg;  t5 = 3.5 * sg;  t6 = 5.0 * sg;
+    }
+    uint32_t word[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double a = (double)fabsf(v[i]);
+      uint32_t c = (a > t0) + (a >= t1) + (a > t2) + (a >= t3) + (a > t4) + (a >= t5) + (a > t6);
+      c |= (__float_as_uint(v[i]) >> 31) << 3;
+      word[i >> 3] |= c << (4 * (i & 7));
+    }
+    *reinterpret_cast<uint2*>(codes + it.r * ld_codes + it.j * 8) = make_uint2(word[0], word[1]);
+    scales[it.r * ld_scales + it.j] = (uint8_t)s;
+  }
+}
+
+}  // namespace
+
+int partial_count(int64_t rows, int64_t cols, int chunk) {
+  const int64_t work = rows * (cols / chunk);
+  int64_t wg = (work + kElemThreads - 1) / kElemThreads;
+  if (wg < 1) wg = 1;
+  if (wg > kMaxPartials) wg = kMaxPartials;
+  return (int)wg;
+}
+
+hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                       float* partials, int n_partials, hipStream_t s) {
+  const int esz = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  const int64_t bpr = cols / 16;
+  if (dtype == NVFP4_DTYPE_BF16)
+    amax_kernel<NVFP4_DTYPE_BF16><<<n_partials, kElemThreads, 0, s>>>(
+        (const uint8_t*)x, ld_x * esz, rows, bpr, partials);
+  else
+    amax_kernel<NVFP4_DTYPE_F32><<<n_partials, kElemThreads, 0, s>>>(
+        (const uint8_t*)x, ld_x * esz, rows, bpr, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                           float* g, int mode, const float* partials, int n_partials,
+                           hipStream_t s) {
+  const int esz = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  const int64_t bpr = cols / 16;
+  // enough workgroups to cover the chip several times, bounded so the
+  // per-workgroup reduction of the partials stays cheap
+  int64_t wg = (rows * bpr + kElemThreads - 1) / kElemThreads;
+  if (wg > 4096) wg = 4096;
+  if (wg < 1) wg = 1;
+  if (dtype == NVFP4_DTYPE_BF16)
+    quantize_kernel<NVFP4_DTYPE_BF16><<<(int)wg, kElemThreads, 0, s>>>(
+        (const uint8_t*)x, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode,
+        partials, n_partials);
+  else
+    quantize_kernel<NVFP4_DTYPE_F32><<<(int)wg, kElemThreads, 0, s>>>(
+        (const uint8_t*)x, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode,
+        partials, n_partials);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

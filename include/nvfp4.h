@@ -1,0 +1,189 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 linear-layer library.
+ *
+ * The operations follow one paper, "Why Gated DeltaNet Survives 4-Bit
+ * Quantization: NVFP4 W4A4 for the Recurrent Half of a Hybrid 27B LLM"
+ * (arXiv 2609.04098), as the web pages about it describe it:
+ *
+ *   - NVFP4 stores E2M1 element codes with one E4M3 scale per 16 elements
+ *     (evolve.pub review, "Scope & Claims"; thevalue.engineering article,
+ *     section on the fragility myth) and one float32 global scale per tensor;
+ *   - weights and activations are both 4-bit on every linear layer, so the
+ *     activations are quantized on the fly before each GEMM (chatpaper.ai
+ *     English abstract; evolve.pub review, "Summary");
+ *   - a fused GEMM over several modules keeps each module's global scale
+ *     (the fused-GEMM global-scale mismatch of the chatpaper.ai abstract and
+ *     the evolve.pub review, "Key claims under review", fourth claim);
+ *   - the GDN gates: write strength through a sigmoid, decay through a
+ *     log-space softplus/exponential (chatpaper.ai abstract, mechanism (ii)).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  Host
+ *     arrays and structs are read only during the call.  The library
+ *     allocates no memory and keeps no mutable global state.
+ *   - Every call enqueues work on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and returns without synchronizing.
+ *   - Matrices are row-major.  An NVFP4 matrix [rows, cols] is:
+ *       codes  uint8 [rows, ld_codes]  two 4-bit codes per byte, element 2j
+ *              in the low nibble of byte j; code = sign<<3 | E2M1 magnitude;
+ *       scales uint8 [rows, ld_scales] one E4M3 (OCP "FN") byte per 16
+ *              consecutive elements of a row;
+ *       global float32, one per tensor (or per weight segment).
+ *     An element decodes to (+-)e2m1 * e4m3 * global.
+ *   - cols must be a multiple of 16.  Row strides: ld_codes >= cols/2 and a
+ *     multiple of 16 bytes, ld_scales >= cols/16 and a multiple of 8 bytes;
+ *     code and scale base pointers 16- and 8-byte aligned.  (Dense layouts
+ *     satisfy this whenever cols % 128 == 0.)
+ *   - Return value: NVFP4_OK (0) or a negative nvfp4_status.  Arguments are
+ *     validated before any HIP call; an invalid call enqueues nothing.  A
+ *     HIP launch error is returned as NVFP4_ERR_HIP and its text is kept for
+ *     nvfp4_status_string.  Device faults surface at the caller's next
+ *     synchronization, as in HIP.  Non-finite inputs are outside the
+ *     contract (results unspecified).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = -1,      /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = -2,     /* rows/cols <= 0, cols % 16 != 0, or mismatched K */
+  NVFP4_ERR_DTYPE = -3,     /* unknown dtype code */
+  NVFP4_ERR_STRIDE = -4,    /* a leading dimension too small or misaligned */
+  NVFP4_ERR_ALIGN = -5,     /* a base pointer misaligned */
+  NVFP4_ERR_SEGMENTS = -6,  /* bad segment table */
+  NVFP4_ERR_GATE = -7,      /* bad gate specification */
+  NVFP4_ERR_WORKSPACE = -8, /* workspace missing or too small */
+  NVFP4_ERR_FLAGS = -9,     /* unknown flag bits */
+  NVFP4_ERR_HIP = -10,      /* a HIP launch failed */
+  NVFP4_ERR_RANGE = -11     /* a size beyond what the kernels index (2^31) */
+} nvfp4_status;
+
+/* Element types of dense (non-NVFP4) operands. */
+enum { NVFP4_DTYPE_BF16 = 0, NVFP4_DTYPE_F32 = 1 };
+
+/* nvfp4_quantize flags. */
+enum {
+  NVFP4_SCALE_DYNAMIC = 0,   /* compute g = fl32(amax / (6*448)) on the device and store it */
+  NVFP4_SCALE_STATIC = 1,    /* read a caller-provided g from *global_scale (calibrated scale) */
+  NVFP4_AMAX_PRECOMPUTED = 2 /* DYNAMIC, but the amax partials are already in the workspace
+                                (written by nvfp4_silu_mul); skips the amax pass */
+};
+
+/* Most segments a fused GEMM accepts. */
+#define NVFP4_MAX_SEGMENTS 16
+
+/* Bytes of device workspace nvfp4_quantize needs for a [rows, cols]
+ * input (per-workgroup amax partials).  Always > 0 and <= 4096. */
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
+
+/*
+ * nvfp4_quantize -- NVFP4-quantize a dense matrix (on-the-fly activation
+ * quantization; also used offline for weights, one call per module).
+ *
+ *   x        device, x_dtype elements [rows, ld_x], 16-byte aligned,
+ *            ld_x * sizeof(elem) a multiple of 16 bytes.
+ *   codes    device uint8 [rows, ld_codes]   (written)
+ *   scales   device uint8 [rows, ld_scales]  (written)
+ *   global_scale device float32[1]: written (DYNAMIC) or read (STATIC).
+ *   workspace device, >= nvfp4_quantize_workspace_bytes(rows, cols) bytes,
+ *            4-byte aligned; its contents need no initialization (DYNAMIC
+ *            only; may be NULL for STATIC).
+ *
+ * Result, bit for bit: g = fl32(amax|x| / 2688) (DYNAMIC); per block of 16,
+ * scale = E4M3 nearest to the exact amax_block / (6 g) (ties to even code,
+ * > 448 saturates, g == 0 or an all-zero block gives 0); per element,
+ * magnitude = E2M1 nearest to the exact |x| / (scale * g) (ties to even,
+ * > 6 saturates, scale 0 gives 0), sign = IEEE sign bit of x.
+ * Two kernel launches (amax pass, quantize pass) on `stream`.
+ */
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                   float* global_scale, int flags, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* An NVFP4 operand of a GEMM (all pointers device). */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* global_scale; /* ignored for the weight of nvfp4_gemm_fused_segments */
+  int64_t rows, cols;
+  int64_t ld_codes, ld_scales;
+} nvfp4_tensor;
+
+/*
+ * nvfp4_gemm -- W4A4 GEMM out[M, N] = g_a * g_w * sum_k dec(a)[m,k] * dec(w)[n,k]
+ * (out = A W^T, as a linear layer), a = activations [M, K], w = weight [N, K].
+ *
+ *   out      device [M, ld_out] of out_dtype (bf16: round to nearest even).
+ * Every decoded operand is exact in fp16; products are exact in fp32 and
+ * are accumulated in fp32 (MFMA).  Agrees with the exact result within
+ * 1e-5 * sum_k |a*w| per element (plus half a bf16 ulp for bf16 output).
+ */
+int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* w, void* out, int out_dtype,
+               int64_t ld_out, void* stream);
+
+/* GDN gate epilogue: columns of segment b_segment become sigmoid(x); columns
+ * of segment a_segment become -exp(A_log[h]) * softplus(x + dt_bias[h]),
+ * h = column - start of a_segment.  x is the scaled fp32 accumulator.
+ * Either segment index may be -1 (absent).  A_log and dt_bias are device
+ * float32 [width of a_segment]; they may be NULL when a_segment == -1. */
+typedef struct {
+  int b_segment;
+  int a_segment;
+  const float* A_log;
+  const float* dt_bias;
+} nvfp4_gdn_gate;
+
+/*
+ * nvfp4_gemm_fused_segments -- one GEMM over a weight made of n_segments
+ * row blocks (modules) concatenated along N, each with its own global scale:
+ *   out[m, n] = g_a * seg_global_scales[s(n)] * sum_k dec(a)[m,k] * dec(w)[n,k]
+ * where s(n) is the segment with seg_offsets[s] <= n < seg_offsets[s+1].
+ * This equals the concatenation of one nvfp4_gemm per segment, and is the
+ * repair of the global-scale mismatch: no segment is served with another
+ * segment's scale.  Then the optional gate epilogue transforms the b/a
+ * segment columns in place.
+ *
+ *   seg_offsets        HOST int64 [n_segments + 1], seg_offsets[0] == 0,
+ *                      strictly increasing, seg_offsets[n] == w->rows.
+ *   seg_global_scales  DEVICE float32 [n_segments].
+ *   gate               HOST pointer, may be NULL (no gate epilogue).
+ * 1 <= n_segments <= NVFP4_MAX_SEGMENTS.
+ */
+int nvfp4_gemm_fused_segments(const nvfp4_tensor* a, const nvfp4_tensor* w, int n_segments,
+                              const int64_t* seg_offsets, const float* seg_global_scales,
+                              const nvfp4_gdn_gate* gate, void* out, int out_dtype, int64_t ld_out,
+                              void* stream);
+
+/*
+ * nvfp4_silu_mul -- MLP glue between the gate_up and down projections:
+ *   h[m, j] = bf16( silu(gu[m, j]) * gu[m, inter + j] ),  j < inter,
+ * evaluated in fp32 from bf16 inputs, rounded to nearest even.
+ *   gu   device bf16 [rows, ld_gu], ld_gu >= 2*inter;  h device bf16 [rows, ld_h].
+ *   inter % 8 == 0; ld_gu, ld_h multiples of 8 elements; 16-byte aligned.
+ *   amax_workspace: NULL, or a workspace of nvfp4_quantize_workspace_bytes(rows,
+ *   inter) bytes that receives the amax partials of h, so that a following
+ *   nvfp4_quantize of h with NVFP4_AMAX_PRECOMPUTED skips its amax pass.
+ */
+int nvfp4_silu_mul(const void* gu, int64_t rows, int64_t inter, int64_t ld_gu, void* h,
+                   int64_t ld_h, void* amax_workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status (and of the last HIP error, for NVFP4_ERR_HIP). */
+const char* nvfp4_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every entry point include/nvfp4.h
+declares, and rejects invalid arguments before any HIP call (CPU only: no
+call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_linear_layer_amd as nv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(nvfp4_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_api():
+    fns = declared_functions()
+    for f in ("nvfp4_quantize", "nvfp4_quantize_workspace_bytes", "nvfp4_gemm",
+              "nvfp4_gemm_fused_segments", "nvfp4_silu_mul", "nvfp4_status_string", "nvfp4_version"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(nv.lib_path)
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+
+
+def test_version_and_status_strings():
+    assert nv.nvfp4_version() >= 100
+    assert nv.nvfp4_status_string(0) == "ok"
+    for code in range(-1, -12, -1):
+        assert nv.nvfp4_status_string(code) not in ("", "unknown status")
+
+
+def test_workspace_bytes():
+    assert nv.nvfp4_quantize_workspace_bytes(1, 16) == 4
+    assert 4 <= nv.nvfp4_quantize_workspace_bytes(32768, 5120) <= 4096
+
+
+FAKE = 1 << 20  # a well-aligned non-null pointer value; never dereferenced on these paths
+
+
+def q(**kw):
+    args = dict(x=FAKE, dt=0, rows=4, cols=32, ldx=32, codes=FAKE, ldc=16, scales=FAKE, lds=8,
+                g=FAKE, flags=0, ws=FAKE, wsb=4096, stream=None)
+    args.update(kw)
+    return nv.load().nvfp4_quantize(args["x"], args["dt"], args["rows"], args["cols"], args["ldx"],
+                                    args["codes"], args["ldc"], args["scales"], args["lds"], args["g"],
+                                    args["flags"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), -1), (dict(codes=None), -1), (dict(g=None), -1),
+    (dict(dt=7), -3), (dict(flags=9), -9),
+    (dict(cols=24, ldx=24), -2), (dict(rows=0), -2), (dict(rows=-3), -2),
+    (dict(ldx=16), -4), (dict(ldc=8), -4), (dict(lds=1), -4),
+    (dict(x=FAKE + 2), -5), (dict(ws=None), -8), (dict(wsb=0), -8),
+    (dict(rows=1 << 31), -11),
+])
+def test_quantize_rejects_bad_arguments(kw, status):
+    assert q(**kw) == status
+
+
+def tensor(rows=4, cols=32, ldc=16, lds=8, codes=FAKE, scales=FAKE, g=FAKE):
+    return nv._Tensor(codes, scales, g, rows, cols, ldc, lds)
+
+
+def gemm(a=None, w=None, out=FAKE, dt=0, ld=8):
+    a = a or tensor()
+    w = w or tensor(rows=8)
+    return nv.load().nvfp4_gemm(ctypes.byref(a), ctypes.byref(w), out, dt, ld, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=tensor(codes=0)), -1), (dict(w=tensor(rows=8, g=0)), -1), (dict(out=None), -1),
+    (dict(a=tensor(cols=48, ldc=32)), -2), (dict(a=tensor(cols=20)), -2),
+    (dict(dt=5), -3), (dict(ld=4), -4), (dict(a=tensor(ldc=24)), -4), (dict(a=tensor(lds=4)), -4),
+    (dict(a=tensor(codes=FAKE + 8)), -5), (dict(out=FAKE + 1), -5),
+])
+def test_gemm_rejects_bad_arguments(kw, status):
+    assert gemm(**kw) == status
+
+
+def fused(nseg=2, offs=(0, 4, 8), gate=None, sg=FAKE):
+    a, w = tensor(), tensor(rows=8)
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    return nv.load().nvfp4_gemm_fused_segments(ctypes.byref(a), ctypes.byref(w), nseg, arr, sg,
+                                               None if gate is None else ctypes.byref(gate), FAKE, 0, 8, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nseg=0, offs=(0,)), -6), (dict(nseg=17, offs=tuple(range(18))), -6),
+    (dict(offs=(0, 4, 7)), -6), (dict(offs=(1, 4, 8)), -6), (dict(offs=(0, 9, 8)), -6),
+    (dict(sg=None), -1),
+    (dict(gate=nv._Gate(2, -1, None, None)), -7), (dict(gate=nv._Gate(0, 0, FAKE, FAKE)), -7),
+    (dict(gate=nv._Gate(0, 1, None, FAKE)), -7),
+])
+def test_fused_rejects_bad_arguments(kw, status):
+    assert fused(**kw) == status
+
+
+def test_silu_mul_rejects_bad_arguments():
+    f = nv.load().nvfp4_silu_mul
+    assert f(None, 4, 16, 32, FAKE, 16, None, 0, None) == -1
+    assert f(FAKE, 4, 12, 32, FAKE, 16, None, 0, None) == -2
+    assert f(FAKE, 4, 16, 24, FAKE, 16, None, 0, None) == -4
+    assert f(FAKE + 4, 4, 16, 32, FAKE, 16, None, 0, None) == -5
+    assert f(FAKE, 4, 16, 32, FAKE, 16, FAKE, 0, None) == -8
+    assert f(FAKE, 4, 8, 16, FAKE, 8, FAKE, 4096, None) == -2  # amax partials need inter % 16 == 0

@@ -1,0 +1,204 @@
+"""GPU parity: W4A4 GEMM, fused segments and the GDN gate epilogue through
+the C ABI, against the oracle's float64 GEMM on the same quantized operands
+(|err| <= 1e-5 * sum|a*w| per element, plus half a bf16 ulp for bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_linear_layer_amd as nv
+import workloads as W
+from oracle import nvfp4_oracle as O
+from tests.gpu_util import (DEV, assert_close, host_q, oracle_weight, quantize_dev, say,
+                            weight_segments)
+
+pytestmark = pytest.mark.gpu
+
+
+def rand_bf16(seed, rows, cols, scale=1.0, outliers=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)) * scale
+    if outliers:
+        x[:, rng.choice(cols, outliers, replace=False)] *= 60
+    return W.to_bf16(x).to(DEV)
+
+
+def run_gemm(x, w, out_dtype):
+    a = quantize_dev(x)
+    wq = quantize_dev(w)
+    out = nv.gemm(a, wq, out_dtype=out_dtype)
+    ac, as_, ag = host_q(a)
+    wc, ws, wg = host_q(wq)
+    ref, tol = O.gemm(ac, as_, ag, wc, ws, wg, x.shape[1])
+    return out, ref, tol
+
+
+SHAPES = [(1, 48, 16), (8, 130, 32), (17, 64, 48), (33, 257, 144), (100, 300, 256),
+          (300, 520, 1040), (256, 256, 128), (513, 384, 640), (32, 128, 256), (64, 96, 5120)]
+
+
+@pytest.mark.parametrize("m,n,k", SHAPES, ids=lambda v: str(v))
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_shapes(m, n, k, out_dtype):
+    say(f"gemm {m}x{n}x{k} {out_dtype}")
+    x = rand_bf16(m * 31 + n, m, k, outliers=min(2, k // 16))
+    w = rand_bf16(n * 17 + k, n, k, 0.02)
+    out, ref, tol = run_gemm(x, w, torch.float32 if out_dtype == "f32" else torch.bfloat16)
+    assert_close(out, ref, tol, out_dtype)
+
+
+def test_tiny_config_fp32():
+    say("gemm tiny 32x128x256")
+    wl = W.tiny()
+    out, ref, tol = run_gemm(wl.x.to(DEV), wl.weights[0][1].to(DEV), torch.float32)
+    assert_close(out, ref, tol, "f32")
+
+
+def test_act_quant_gemm_full_size():
+    say("gemm act_quant_gemm 4096x5120x5120")
+    wl = W.act_quant_gemm()
+    out, ref, tol = run_gemm(wl.x.to(DEV), wl.weights[0][1].to(DEV), torch.bfloat16)
+    assert_close(out, ref, tol, "bf16")
+
+
+def test_accumulation_stress_all_positive():
+    """All-positive operands at K = 17408: no cancellation, the fp32
+    accumulation error is at its relative worst."""
+    say("gemm all-positive K=17408")
+    rng = np.random.default_rng(5)
+    x = W.to_bf16(np.abs(rng.standard_normal((64, 17408)))).to(DEV)
+    w = W.to_bf16(np.abs(rng.normal(0, 0.02, (256, 17408)))).to(DEV)
+    out, ref, tol = run_gemm(x, w, torch.float32)
+    ratio = assert_close(out, ref, tol, "f32")
+    say(f"  worst err / tolerance = {ratio:.3f}")
+
+
+def test_output_canaries_and_determinism():
+    """Stores stay inside [M, N] of a strided output, and two runs agree
+    bit for bit."""
+    say("gemm canaries")
+    m, n, k = 77, 200, 384
+    x = rand_bf16(1, m, k)
+    w = rand_bf16(2, n, k, 0.02)
+    a, wq = quantize_dev(x), quantize_dev(w)
+    big = torch.full((m + 5, n + 24), 12345.0, dtype=torch.float32, device=DEV)
+    view = big[:m, :n]
+    nv.nvfp4_gemm(a, wq, view)
+    torch.cuda.synchronize()
+    assert torch.all(big[m:] == 12345.0) and torch.all(big[:, n:] == 12345.0)
+    again = nv.gemm(a, wq, out_dtype=torch.float32)
+    assert torch.equal(again, view)
+    ac, as_, ag = host_q(a)
+    wc, ws, wg = host_q(wq)
+    ref, tol = O.gemm(ac, as_, ag, wc, ws, wg, k)
+    assert_close(view, ref, tol, "f32")
+
+
+# ------------------------------------------------------------ segments
+
+
+def small_gdn(m=200, scale_rows=1 / 64):
+    wl = W.gdn_in_proj(seed=0, m=m, k=512, scale_rows=scale_rows)
+    x = wl.x.to(DEV)
+    wq, offs, seg_g = weight_segments([(n, w.to(DEV)) for n, w in wl.weights])
+    return wl, x, wq, offs, seg_g
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_fused_segments_with_gates(out_dtype):
+    say(f"fused GDN small {out_dtype}")
+    wl, x, wq, offs, seg_g = small_gdn()
+    a = quantize_dev(x)
+    gate = dict(b_segment=4, a_segment=5, A_log=wl.extra["A_log"].to(DEV), dt_bias=wl.extra["dt_bias"].to(DEV))
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out = nv.gemm_fused_segments(a, wq, offs, seg_g, gate=gate, out_dtype=tdt)
+    ac, as_, ag = host_q(a)
+    wc, ws, sg = oracle_weight(wq, offs, seg_g)
+    ref, tol = O.fused_segments(ac, as_, ag, wc, ws, offs, sg, x.shape[1])
+    o = out.float().cpu().numpy()
+    # linear segments
+    lin = slice(0, offs[4])
+    assert_close(out[:, lin], ref[:, lin], tol[:, lin], out_dtype, "fused linear segments")
+    # gates
+    a_log = wl.extra["A_log"].numpy().astype(np.float64)
+    dt_bias = wl.extra["dt_bias"].numpy().astype(np.float64)
+    bsl, asl = slice(offs[4], offs[5]), slice(offs[5], offs[6])
+    beta, tb, _, _ = O.gate_tolerances(ref[:, bsl], tol[:, bsl], a_log, dt_bias)
+    _, _, dec, td = O.gate_tolerances(ref[:, asl], tol[:, asl], a_log, dt_bias)
+    assert_close(out[:, bsl], beta, tb, out_dtype, "sigmoid gate")
+    assert_close(out[:, asl], dec, td, out_dtype, "decay gate")
+    assert np.all(o[:, asl] < 0) and np.all((o[:, bsl] >= 0) & (o[:, bsl] <= 1))
+
+
+def test_fused_equals_per_segment_gemms():
+    say("fused == concat")
+    wl, x, wq, offs, seg_g = small_gdn(m=96)
+    a = quantize_dev(x)
+    fused = nv.gemm_fused_segments(a, wq, offs, seg_g, out_dtype=torch.float32)
+    for s in range(len(offs) - 1):
+        part = wq.row_slice(offs[s], offs[s + 1])
+        part = nv.NVFP4Tensor(part.codes, part.scales, seg_g[s:s + 1], part.rows, part.cols)
+        single = nv.gemm(a, part, out_dtype=torch.float32)
+        d = (single - fused[:, offs[s]:offs[s + 1]]).abs().max().item()
+        scale = single.abs().max().item()
+        assert d <= 1e-5 * max(scale, 1e-30), (s, d, scale)
+
+
+def test_single_global_scale_mismatch_is_detected():
+    """Serving the fused weight with one module's global scale (the
+    mismatch) puts every other segment off by g_w[0]/g_w[s]."""
+    say("fused mismatch negative test")
+    wl, x, wq, offs, seg_g = small_gdn(m=64)
+    a = quantize_dev(x)
+    good = nv.gemm_fused_segments(a, wq, offs, seg_g, out_dtype=torch.float32)
+    bad = nv.gemm_fused_segments(a, wq, offs, seg_g[:1].repeat(len(offs) - 1).contiguous(), out_dtype=torch.float32)
+    g = seg_g.cpu().numpy()
+    off_by_far = 0
+    for s in range(1, len(offs) - 1):
+        sl = slice(offs[s], offs[s + 1])
+        ratio = float(g[0]) / float(g[s])
+        assert torch.allclose(bad[:, sl], good[:, sl] * ratio, rtol=1e-5, atol=1e-30)
+        if abs(ratio - 1) > 0.05:  # far outside the GEMM tolerance
+            off_by_far += 1
+            assert not torch.allclose(bad[:, sl], good[:, sl], rtol=1e-3, atol=0)
+    assert off_by_far >= 3  # the wide-sigma segments really differ in scale
+
+
+def test_gdn_in_proj_full_size_sampled_rows():
+    """32768 x 16480 x 5120 fused GDN in-projection with the gate epilogue:
+    256 sampled rows (first and last row tiles included) against the
+    oracle."""
+    say("fused GDN 32768x16480x5120 sampled")
+    wl = W.gdn_in_proj()
+    x = wl.x.to(DEV)
+    wq, offs, seg_g = weight_segments([(n, w.to(DEV)) for n, w in wl.weights])
+    a = quantize_dev(x)
+    gate = dict(b_segment=4, a_segment=5, A_log=wl.extra["A_log"].to(DEV), dt_bias=wl.extra["dt_bias"].to(DEV))
+    out = nv.gemm_fused_segments(a, wq, offs, seg_g, gate=gate, out_dtype=torch.bfloat16)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 32767], np.random.default_rng(2).integers(0, 32768, 251)]))
+    ac, as_, ag = host_q(a)
+    wc, ws, sg = oracle_weight(wq, offs, seg_g)
+    ref, tol = O.fused_segments(ac[rows], as_[rows], ag, wc, ws, offs, sg, 5120)
+    o = out[torch.from_numpy(rows).to(DEV)]
+    lin = slice(0, offs[4])
+    assert_close(o[:, lin], ref[:, lin], tol[:, lin], "bf16", "GDN q/k/v/z")
+    a_log = wl.extra["A_log"].numpy().astype(np.float64)
+    dt_bias = wl.extra["dt_bias"].numpy().astype(np.float64)
+    bsl, asl = slice(offs[4], offs[5]), slice(offs[5], offs[6])
+    beta, tb, _, _ = O.gate_tolerances(ref[:, bsl], tol[:, bsl], a_log, dt_bias)
+    _, _, dec, td = O.gate_tolerances(ref[:, asl], tol[:, asl], a_log, dt_bias)
+    assert_close(o[:, bsl], beta, tb, "bf16", "b gate")
+    assert_close(o[:, asl], dec, td, "bf16", "a gate")
+
+
+def test_decode_full_size():
+    """M = 8 tokens x the fused gate_up weight [34816, 5120] (two segments)."""
+    say("decode 8x34816x5120")
+    wl = W.decode()
+    x = wl.x.to(DEV)
+    wq, offs, seg_g = weight_segments([(n, w.to(DEV)) for n, w in wl.weights])
+    a = quantize_dev(x)
+    out = nv.gemm_fused_segments(a, wq, offs, seg_g, out_dtype=torch.bfloat16)
+    ac, as_, ag = host_q(a)
+    wc, ws, sg = oracle_weight(wq, offs, seg_g)
+    ref, tol = O.fused_segments(ac, as_, ag, wc, ws, offs, sg, 5120)
+    assert_close(out, ref, tol, "bf16", "decode")
