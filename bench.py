@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 W4A4 linear-layer hot path on one MI355X.
+
+One step = one pass of the whole path over the 8192-token MLP pair: dynamic
+NVFP4 quantization of X [8192, 5120] -> fused gate|up GEMM (two segments,
+each with its own global scale) -> SiLU*mul (+ amax partials) ->
+quantization of h [8192, 17408] -> down GEMM.  Every step runs in the
+library's HIP kernels on torch's current stream; inputs are synthetic,
+seeded and resident in HBM before the timed region.
+
+Prints ONE JSON line: TFLOP/s including activation quantization (algorithmic
+2*M*N*K of both GEMMs over the time of every stage), the roofline of the
+dominant kernel (the gate|up GEMM, timed live with HIP events on the launch
+stream), the decode-shape (M=8) weight-streaming GB/s, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 W4A4 GEMM TFLOP/s incl. act-quant (M=8192) + % peak; GB/s at M=8"
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_m8192_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "bit_linear_layer_amd", "csrc", "gemm.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the decode / GDN measurements")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch of the gate|up GEMM from the committed rocprofv3
+    counter summary, or None if absent or taken on another kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256") != sha256(GEMM_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards without communication along N; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_linear_layer_amd as nv
+    import workloads as W
+
+    nv.load()  # fails loudly without the HIP library
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ inputs
+    log("generating the 8192-token MLP pair workload (seed 0)")
+    wl = W.mlp_pair()
+    m, k = wl.x.shape
+    inter = wl.weights[0][1].shape[0]
+    x = wl.x.to(dev)
+
+    def quant_segments(segs):
+        rows = sum(w.shape[0] for w in segs)
+        kk = segs[0].shape[1]
+        q = nv.empty_nvfp4(rows, kk, dev)
+        g = torch.empty(len(segs), dtype=torch.float32, device=dev)
+        ws = nv.workspace_for(max(w.shape[0] for w in segs), kk, dev)
+        offs = [0]
+        for s, w in enumerate(segs):
+            part = q.row_slice(offs[-1], offs[-1] + w.shape[0])
+            nv.nvfp4_quantize(w.to(dev), nv.NVFP4Tensor(part.codes, part.scales, g[s:s + 1], part.rows, kk),
+                              nv.SCALE_DYNAMIC, ws)
+            offs.append(offs[-1] + w.shape[0])
+        return q, offs, g
+
+    w_gu, gu_offs, gu_g = quant_segments([w for _, w in wl.weights])  # offline, untimed
+    w_d, d_offs, d_g = quant_segments([wl.extra["w_down"]])
+    a = nv.empty_nvfp4(m, k, dev)
+    hq = nv.empty_nvfp4(m, inter, dev)
+    gu = torch.empty((m, 2 * inter), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((m, inter), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    ws_x = nv.workspace_for(m, k, dev)
+    ws_h = nv.workspace_for(m, inter, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        nv.nvfp4_quantize(x, a, nv.SCALE_DYNAMIC, ws_x)
+        if ev is not None:
+            ev[0].record(stream)
+        nv.nvfp4_gemm_fused_segments(a, w_gu, gu_offs, gu_g, gu)
+        if ev is not None:
+            ev[1].record(stream)
+        nv.nvfp4_silu_mul(gu, h, inter, ws_h)
+        nv.nvfp4_quantize(h, hq, nv.AMAX_PRECOMPUTED, ws_h)
+        nv.nvfp4_gemm_fused_segments(hq, w_d, d_offs, d_g, out)
+
+    flops_gu = 2.0 * m * (2 * inter) * k
+    flops_d = 2.0 * m * k * inter
+    flops = flops_gu + flops_d
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = t0.elapsed_time(t1)
+    ms_per_step = elapsed_ms / args.steps
+    value = flops * args.steps / (elapsed_ms * 1e-3) / 1e12
+    gu_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    achieved = flops_gu / (gu_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    roofline = {"bound": "mfma", "kernel": "nvfp4 gemm (gate|up, 8192x34816x5120)",
+                "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "avg_launch_ms": round(gu_ms, 4)}
+    log(f"step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; gate|up GEMM {gu_ms:.3f} ms = {achieved:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1+e4m3) -> f16 mfma, f32 accumulate",
+        "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": wl.name, "M": m, "K": k, "inter": inter,
+                   "gate_up": [2 * inter, k], "down": [k, inter], "parallelism": "single-gpu"},
+        "pct_of_mfma_peak": round(100.0 * value / MFMA_F16_PEAK_TFLOPS, 2),
+        "roofline": roofline,
+    }
+
+    # --------------------------------------------- decode shape (M = 8)
+    if not args.no_secondary:
+        result["secondary"] = secondary(nv, W, torch, np, dev, stream, log)
+
+    # --------------------------------------------------- CPU oracle leg
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(nv, W, torch, np, wl, a, w_gu, gu_offs, gu_g, w_d, d_offs, d_g,
+                                              args.cpu_rows, log)
+    print(json.dumps(result), flush=True)
+
+
+def secondary(nv, W, torch, np, dev, stream, log):
+    """Decode-shape weight streaming (M=8 x [34816, 5120], four rotating
+    weight copies so reads come from HBM, not the 256 MB MALL) and the
+    32768-token fused GDN in-projection with gates."""
+    res = {}
+    log("decode M=8 x 34816x5120: four rotating NVFP4 weight copies")
+    dw = W.decode()
+    xd = dw.x.to(dev)
+    segs = [w for _, w in dw.weights]
+    rows = sum(w.shape[0] for w in segs)
+    kk = segs[0].shape[1]
+    base = nv.empty_nvfp4(rows, kk, dev)
+    g = torch.empty(len(segs), dtype=torch.float32, device=dev)
+    ws = nv.workspace_for(segs[0].shape[0], kk, dev)
+    offs = [0]
+    for s, w in enumerate(segs):
+        part = base.row_slice(offs[-1], offs[-1] + w.shape[0])
+        nv.nvfp4_quantize(w.to(dev), nv.NVFP4Tensor(part.codes, part.scales, g[s:s + 1], part.rows, kk),
+                          nv.SCALE_DYNAMIC, ws)
+        offs.append(offs[-1] + w.shape[0])
+    copies = [base] + [nv.NVFP4Tensor(base.codes.clone(), base.scales.clone(), base.global_scale, rows, kk)
+                       for _ in range(3)]
+    ad = nv.quantize(xd)
+    outd = torch.empty((xd.shape[0], rows), dtype=torch.bfloat16, device=dev)
+    wsd = nv.workspace_for(xd.shape[0], kk, dev)
+    iters = 200
+    for i in range(8):
+        nv.nvfp4_gemm_fused_segments(ad, copies[i % 4], offs, g, outd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        nv.nvfp4_gemm_fused_segments(ad, copies[i % 4], offs, g, outd)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_gemm = e0.elapsed_time(e1) / iters * 1e-3
+    m = xd.shape[0]
+    alg_bytes = rows * kk // 2 + rows * kk // 16 + m * kk // 2 + m * kk // 16 + m * rows * 2
+    e0.record(stream)
+    for i in range(iters):
+        nv.nvfp4_quantize(xd, ad, nv.SCALE_DYNAMIC, wsd)
+        nv.nvfp4_gemm_fused_segments(ad, copies[i % 4], offs, g, outd)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_full = e0.elapsed_time(e1) / iters * 1e-3
+    res["decode_m8"] = {"workload": dw.name, "gemm_us": round(t_gemm * 1e6, 2),
+                        "gemm_GBps": round(alg_bytes / t_gemm / 1e9, 1),
+                        "frac_of_hbm_peak": round(alg_bytes / t_gemm / 1e9 / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes": alg_bytes, "quantize_plus_gemm_us": round(t_full * 1e6, 2)}
+    log(f"decode: gemm {t_gemm * 1e6:.1f} us = {alg_bytes / t_gemm / 1e9:.0f} GB/s")
+    del copies, base, outd
+
+    log("fused GDN in-projection 32768 x 16480 x 5120 with gates")
+    gw = W.gdn_in_proj()
+    xg = gw.x.to(dev)
+    segs = [w for _, w in gw.weights]
+    rows = sum(w.shape[0] for w in segs)
+    wq = nv.empty_nvfp4(rows, kk, dev)
+    sg = torch.empty(len(segs), dtype=torch.float32, device=dev)
+    offs = [0]
+    ws = nv.workspace_for(max(w.shape[0] for w in segs), kk, dev)
+    for s, w in enumerate(segs):
+        part = wq.row_slice(offs[-1], offs[-1] + w.shape[0])
+        nv.nvfp4_quantize(w.to(dev), nv.NVFP4Tensor(part.codes, part.scales, sg[s:s + 1], part.rows, kk),
+                          nv.SCALE_DYNAMIC, ws)
+        offs.append(offs[-1] + w.shape[0])
+    gate = dict(b_segment=4, a_segment=5, A_log=gw.extra["A_log"].to(dev), dt_bias=gw.extra["dt_bias"].to(dev))
+    ag = nv.empty_nvfp4(xg.shape[0], kk, dev)
+    wsg = nv.workspace_for(xg.shape[0], kk, dev)
+    outg = torch.empty((xg.shape[0], rows), dtype=torch.bfloat16, device=dev)
+
+    def gstep():
+        nv.nvfp4_quantize(xg, ag, nv.SCALE_DYNAMIC, wsg)
+        nv.nvfp4_gemm_fused_segments(ag, wq, offs, sg, outg, gate)
+    for _ in range(2):
+        gstep()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        gstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 5 * 1e-3
+    fl = 2.0 * xg.shape[0] * rows * kk
+    res["gdn_in_proj_m32768"] = {"workload": gw.name, "ms": round(t * 1e3, 3),
+                                 "TFLOPs_incl_act_quant": round(fl / t / 1e12, 1),
+                                 "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+    log(f"gdn in-proj: {t * 1e3:.3f} ms = {fl / t / 1e12:.0f} TFLOP/s")
+    return res
+
+
+def cpu_baseline(nv, W, torch, np, wl, a, w_gu, gu_offs, gu_g, w_d, d_offs, d_g, rows, log):
+    """The oracle, as it stands, on the first `rows` rows of the same MLP
+    pair step (quantize X rows with the step's global scale, fused gate|up,
+    SiLU*mul, quantize h rows, down), on the host's cores."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import nvfp4_oracle as O
+
+    torch.cuda.synchronize()
+    k = a.cols
+    inter = w_d.cols
+    xs = W.bf16_to_f32_numpy(wl.x[:rows])
+    g_x = np.float32(a.global_scale.cpu().numpy()[0])
+    wgc = w_gu.codes[:, : k // 2].cpu().numpy()
+    wgs = w_gu.scales[:, : k // 16].cpu().numpy()
+    wdc = w_d.codes[:, : inter // 2].cpu().numpy()
+    wds = w_d.scales[:, : inter // 16].cpu().numpy()
+    gg = gu_g.cpu().numpy()
+    dg = d_g.cpu().numpy()
+    log(f"cpu oracle on {rows} rows of the step")
+    t0 = time.perf_counter()
+    ac, as_, ag = O.quantize(xs, g_x)
+    gu, _ = O.fused_segments(ac, as_, ag, wgc, wgs, gu_offs, gg, k, with_tol=False)
+    hh = O.silu_mul(O.round_bf16(gu[:, :inter]), O.round_bf16(gu[:, inter:]))
+    hc, hs, hg = O.quantize(hh.astype(np.float32))
+    out, _ = O.fused_segments(hc, hs, hg, wdc, wds, d_offs, dg, inter, with_tol=False)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * (2 * inter * k + k * inter)
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    log(f"cpu oracle: {dt:.1f} s")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {rows} of 8192 rows of the MLP pair step (quantize X, fused gate|up, "
+                      f"SiLU*mul, quantize h, down) in float64 numpy; weight dequantization inside "
+                      f"each GEMM call as the oracle does it; host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+if __name__ == "__main__":
+    main()

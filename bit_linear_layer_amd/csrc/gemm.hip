@@ -110,27 +110,72 @@ __device__ inline float sigmoidf_(float x) {
 }
 __device__ inline float softplusf_(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
 
-// Stage one K tile of A and W into registers.
+// Stage one K tile of A and W into registers.  Row pointers (rows beyond
+// M or N clamped to the last row: their results are never stored) and LDS
+// destinations are computed once; a K tile advances them by 64 code bytes
+// and 8 scale bytes.  Only the last, partial K tile takes the masked path.
 template <class C>
 struct TileLoader {
   u32x4 chunk[C::kChunkIters];
   uint2 sc[C::kScaleIters];
+  const uint8_t* cptr[C::kChunkIters];
+  const uint8_t* sptr[C::kScaleIters];
+  int cdst[C::kChunkIters];
+  int sdst[C::kScaleIters];
 
-  __device__ void load(const GemmArgs& p, int m0, int n0, int kt) {
-    const int k0 = kt * kBK;
+  __device__ void init(const GemmArgs& p, int m0, int n0, int n_hi) {
 #pragma unroll
     for (int it = 0; it < C::kChunkIters; ++it) {
       const int id = it * C::kThreads + (int)threadIdx.x;
+      const int cid = id < C::kChunks ? id : 0;
+      const bool isB = cid >= C::BM * 4;
+      const int lid = isB ? cid - C::BM * 4 : cid;
+      const int row = lid >> 2, q = lid & 3;
+      const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+      cptr[it] = (isB ? p.w_codes + (int64_t)grow * p.ldw_c : p.a_codes + (int64_t)grow * p.lda_c) + q * 16;
+      cdst[it] = (isB ? C::kACode : 0) + code_slot(row, q);
+    }
+#pragma unroll
+    for (int it = 0; it < C::kScaleIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
+      const int sid = id < C::BM + C::BN ? id : 0;
+      const bool isB = sid >= C::BM;
+      const int row = isB ? sid - C::BM : sid;
+      const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+      sptr[it] = isB ? p.w_scales + (int64_t)grow * p.ldw_s : p.a_scales + (int64_t)grow * p.lda_s;
+      sdst[it] = C::kACode + C::kBCode + (isB ? C::kAScale : 0) + scale_slot(row, 0);
+    }
+  }
+
+  __device__ static bool active_chunk(int it) {
+    return C::kChunks % C::kThreads == 0 || it * C::kThreads + (int)threadIdx.x < C::kChunks;
+  }
+  __device__ static bool active_scale(int it) {
+    return (C::BM + C::BN) % C::kThreads == 0 || it * C::kThreads + (int)threadIdx.x < C::BM + C::BN;
+  }
+
+  // A full K tile (k0 + 128 <= K): unmasked vector loads.
+  __device__ void load_full(int kt) {
+#pragma unroll
+    for (int it = 0; it < C::kChunkIters; ++it)
+      if (active_chunk(it)) chunk[it] = *reinterpret_cast<const u32x4*>(cptr[it] + kt * kRowCodeBytes);
+#pragma unroll
+    for (int it = 0; it < C::kScaleIters; ++it)
+      if (active_scale(it)) sc[it] = *reinterpret_cast<const uint2*>(sptr[it] + kt * kRowScaleBytes);
+  }
+
+  // The last K tile when K % 128 != 0: zero everything beyond K (a zero
+  // code and a zero scale byte both decode to 0).
+  __device__ void load_tail(const GemmArgs& p, int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int it = 0; it < C::kChunkIters; ++it) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (id < C::kChunks) {
-        const bool isB = id >= C::BM * 4;
-        const int lid = isB ? id - C::BM * 4 : id;
-        const int row = lid >> 2, q = lid & 3;
-        const int grow = isB ? min(n0 + row, p.N - 1) : min(m0 + row, p.M - 1);
-        const uint8_t* base = isB ? p.w_codes + (int64_t)grow * p.ldw_c : p.a_codes + (int64_t)grow * p.lda_c;
-        const int kk = k0 + q * 32;  // first element of the chunk
-        const int rem = p.K - kk;
-        const uint8_t* src = base + (kk >> 1);
+      if (active_chunk(it)) {
+        const int id = it * C::kThreads + (int)threadIdx.x;
+        const int q = id & 3;  // chunk ids of A and B both start at multiples of 4
+        const int rem = p.K - (k0 + q * 32);
+        const uint8_t* src = cptr[it] + kt * kRowCodeBytes;
         if (rem >= 32) {
           v = *reinterpret_cast<const u32x4*>(src);
         } else if (rem > 0) {  // rem == 16: the first 8 bytes only
@@ -141,54 +186,37 @@ struct TileLoader {
       }
       chunk[it] = v;
     }
+    const int nb = (p.K >> 4) - kt * kRowScaleBytes;  // valid scale bytes in this tile (1..7)
 #pragma unroll
     for (int it = 0; it < C::kScaleIters; ++it) {
-      const int id = it * C::kThreads + (int)threadIdx.x;
-      uint2 v = make_uint2(0u, 0u);
-      if (id < C::BM + C::BN) {
-        const bool isB = id >= C::BM;
-        const int row = isB ? id - C::BM : id;
-        const int grow = isB ? min(n0 + row, p.N - 1) : min(m0 + row, p.M - 1);
-        const uint8_t* src = (isB ? p.w_scales + (int64_t)grow * p.ldw_s : p.a_scales + (int64_t)grow * p.lda_s) + kt * kRowScaleBytes;
-        const int nb = (p.K >> 4) - kt * kRowScaleBytes;  // valid scale bytes from here
-        if (nb >= 8) {
-          v = *reinterpret_cast<const uint2*>(src);
-        } else {
-          uint32_t lo = 0, hi = 0;
-          for (int b = 0; b < nb; ++b) {
-            const uint32_t byte = src[b];
-            if (b < 4) lo |= byte << (8 * b);
-            else hi |= byte << (8 * (b - 4));
-          }
-          v = make_uint2(lo, hi);
+      uint32_t lo = 0, hi = 0;
+      if (active_scale(it)) {
+        const uint8_t* src = sptr[it] + kt * kRowScaleBytes;
+        for (int b = 0; b < nb; ++b) {
+          const uint32_t byte = src[b];
+          if (b < 4) lo |= byte << (8 * b);
+          else hi |= byte << (8 * (b - 4));
         }
       }
-      sc[it] = v;
+      sc[it] = make_uint2(lo, hi);
     }
+  }
+
+  __device__ void load(const GemmArgs& p, int kt) {
+    if ((kt + 1) * kBK <= p.K) load_full(kt);
+    else load_tail(p, kt);
   }
 
   __device__ void store(uint8_t* stage) const {
 #pragma unroll
-    for (int it = 0; it < C::kChunkIters; ++it) {
-      const int id = it * C::kThreads + (int)threadIdx.x;
-      if (id < C::kChunks) {
-        const bool isB = id >= C::BM * 4;
-        const int lid = isB ? id - C::BM * 4 : id;
-        uint8_t* dst = stage + (isB ? C::kACode : 0) + code_slot(lid >> 2, lid & 3);
-        *reinterpret_cast<u32x4*>(dst) = chunk[it];
-      }
-    }
+    for (int it = 0; it < C::kChunkIters; ++it)
+      if (active_chunk(it)) *reinterpret_cast<u32x4*>(stage + cdst[it]) = chunk[it];
 #pragma unroll
-    for (int it = 0; it < C::kScaleIters; ++it) {
-      const int id = it * C::kThreads + (int)threadIdx.x;
-      if (id < C::BM + C::BN) {
-        const bool isB = id >= C::BM;
-        const int row = isB ? id - C::BM : id;
-        uint8_t* reg = stage + C::kACode + C::kBCode + (isB ? C::kAScale : 0);
-        *reinterpret_cast<uint32_t*>(reg + scale_slot(row, 0)) = sc[it].x;
-        *reinterpret_cast<uint32_t*>(reg + scale_slot(row, 1)) = sc[it].y;
+    for (int it = 0; it < C::kScaleIters; ++it)
+      if (active_scale(it)) {
+        *reinterpret_cast<uint32_t*>(stage + sdst[it]) = sc[it].x;
+        *reinterpret_cast<uint32_t*>(stage + sdst[it] + 128) = sc[it].y;  // h = 1: 32 lanes on
       }
-    }
   }
 };
 
@@ -210,15 +238,18 @@ __device__ inline void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, i
   tn = in / gm;
 }
 
-template <class C>
+// One launch covers the output columns [n_lo, n_hi).  GATE selects the
+// instantiation with the gate epilogue; the host launches it only over the
+// gate segments' columns, so the bulk of the output runs gate-free code.
+template <class C, bool GATE>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_kernel(const GemmArgs p) {
+void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
-  const int tiles_n = (p.N + C::BN - 1) / C::BN;
+  const int tiles_n = (n_hi - n_lo + C::BN - 1) / C::BN;
   int tm, tn;
   tile_of((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int m0 = tm * C::BM, n0 = n_lo + tn * C::BN;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -235,12 +266,13 @@ void gemm_kernel(const GemmArgs p) {
 
   const int nk = (p.K + kBK - 1) / kBK;
   TileLoader<C> ld;
-  ld.load(p, m0, n0, 0);
+  ld.init(p, m0, n0, n_hi);
+  ld.load(p, 0);
   ld.store(smem);
   __syncthreads();
 
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) ld.load(p, m0, n0, kt + 1);
+    if (kt + 1 < nk) ld.load(p, kt + 1);
     const uint8_t* st = smem + (kt & 1) * C::kStage;
     const uint8_t* sA = st;
     const uint8_t* sB = st + C::kACode;
@@ -289,55 +321,81 @@ void gemm_kernel(const GemmArgs p) {
     __syncthreads();
   }
 
-  // Epilogue: per output column its segment's global scale, then the gates.
+  // Epilogue: per output column its segment's global scale (and gate).
   const float ga = *p.ep.a_g;
+  float colscale[C::FN], alog[C::FN], dtb[C::FN];
+  int coln[C::FN], kind[C::FN];
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) {
     const int n = n0 + (fn0 + j) * 32 + (lane & 31);
-    if (n >= p.N) continue;
+    coln[j] = n;
     int seg = 0;
     for (int s = 1; s < p.ep.n_seg; ++s) seg += (n >= p.ep.seg_off[s]) ? 1 : 0;
-    const float sc = ga * p.ep.seg_g[seg];
-    const int kind = seg == p.ep.b_seg ? 1 : (seg == p.ep.a_seg ? 2 : 0);
-    float alog = 0.0f, dtb = 0.0f;
-    if (kind == 2) {
-      const int h = n - p.ep.seg_off[seg];
-      alog = expf(p.ep.A_log[h]);
-      dtb = p.ep.dt_bias[h];
+    colscale[j] = ga * p.ep.seg_g[seg];
+    kind[j] = 0;
+    alog[j] = 0.0f;
+    dtb[j] = 0.0f;
+    if constexpr (GATE) {
+      kind[j] = (seg == p.ep.b_seg) ? 1 : (seg == p.ep.a_seg ? 2 : 0);
+      if (kind[j] == 2 && n < n_hi) {
+        const int h = n - p.ep.seg_off[seg];
+        alog[j] = expf(p.ep.A_log[h]);
+        dtb[j] = p.ep.dt_bias[h];
+      }
     }
+  }
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-      const int mb = m0 + (fm0 + i) * 32 + 4 * (lane >> 5);
+  for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = acc[i][j][r] * colscale[j];
+        if constexpr (GATE) {
+          // one exp and one log1p per element: sigmoid(x) = 1/(1+e^-x),
+          // softplus(z) = max(z,0) + log1p(e^-|z|), with t = x or z
+          const float t = kind[j] == 2 ? x + dtb[j] : x;
+          const float e = expf(-fabsf(t));
+          const float sig = (t >= 0.0f ? 1.0f : e) / (1.0f + e);
+          const float dec = -alog[j] * (fmaxf(t, 0.0f) + log1pf(e));
+          acc[i][j][r] = kind[j] == 1 ? sig : (kind[j] == 2 ? dec : x);
+        } else {
+          acc[i][j][r] = x;
+        }
+      }
+  const bool full_tile = m0 + C::BM <= p.M && n0 + C::BN <= n_hi;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int mb = m0 + (fm0 + i) * 32 + 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int n = coln[j];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = mb + 8 * (r >> 2) + (r & 3);
-        if (m >= p.M) continue;
-        float v = acc[i][j][r] * sc;
-        if (kind == 1) v = sigmoidf_(v);
-        else if (kind == 2) v = -alog * softplusf_(v + dtb);
-        if (p.out_bf16)
-          reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.ld_out + n] = (uint16_t)f32_to_bf16_bits(v);
-        else
-          reinterpret_cast<float*>(p.out)[(int64_t)m * p.ld_out + n] = v;
+        if (full_tile || (m < p.M && n < n_hi)) {
+          const float v = acc[i][j][r];
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.ld_out + n] = (uint16_t)f32_to_bf16_bits(v);
+          else
+            reinterpret_cast<float*>(p.out)[(int64_t)m * p.ld_out + n] = v;
+        }
       }
     }
   }
 }
 
-template <class C>
-hipError_t launch_cfg(const GemmArgs& p, hipStream_t s) {
+template <class C, bool GATE>
+hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
-  const int tiles_n = (p.N + C::BN - 1) / C::BN;
+  const int tiles_n = (n_hi - n_lo + C::BN - 1) / C::BN;
   const int64_t nblocks = (int64_t)tiles_m * tiles_n;
   const size_t lds = 2 * (size_t)C::kStage;
-  static bool attr_done = false;  // raising the dynamic-LDS limit is idempotent
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  gemm_kernel<C><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p);
+  // raising the dynamic-LDS limit is idempotent and cheap
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C, GATE>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  gemm_kernel<C, GATE><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p, n_lo, n_hi);
   return hipGetLastError();
 }
 
@@ -350,14 +408,61 @@ double fill(int64_t tiles) {
   return (double)tiles / (double)(waves * 256);
 }
 
+hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s) {
+  const int n = n_hi - n_lo;
+  if (gate) {
+    if (p.M <= 32) return launch_cfg<CfgS, true>(p, n_lo, n_hi, s);
+    return launch_cfg<CfgM, true>(p, n_lo, n_hi, s);
+  }
+  if (p.M <= 32) return launch_cfg<CfgS, false>(p, n_lo, n_hi, s);
+  const int64_t tl = (int64_t)((p.M + 255) / 256) * ((n + 255) / 256);
+  const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((n + 127) / 128);
+  if (p.M >= 256 && n >= 256 && fill(tl) >= 0.8 * fill(tmd)) return launch_cfg<CfgL, false>(p, n_lo, n_hi, s);
+  return launch_cfg<CfgM, false>(p, n_lo, n_hi, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {
-  if (p.M <= 32) return launch_cfg<CfgS>(p, s);
-  const int64_t tl = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
-  const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128);
-  if (p.M >= 256 && p.N >= 256 && fill(tl) >= 0.8 * fill(tmd)) return launch_cfg<CfgL>(p, s);
-  return launch_cfg<CfgM>(p, s);
+  // Split the columns into maximal runs that are all gate columns or all
+  // gate-free, and launch each run with the matching instantiation.
+  int cuts[2 * NVFP4_MAX_SEGMENTS + 2];
+  int ncut = 0;
+  cuts[ncut++] = 0;
+  for (int g = 0; g < 2; ++g) {
+    const int seg = g == 0 ? p.ep.b_seg : p.ep.a_seg;
+    if (seg < 0) continue;
+    cuts[ncut++] = p.ep.seg_off[seg];
+    cuts[ncut++] = p.ep.seg_off[seg + 1];
+  }
+  cuts[ncut++] = p.N;
+  for (int i = 1; i < ncut; ++i)  // insertion sort of <= 6 cut points
+    for (int j = i; j > 0 && cuts[j] < cuts[j - 1]; --j) {
+      const int t = cuts[j];
+      cuts[j] = cuts[j - 1];
+      cuts[j - 1] = t;
+    }
+  auto gated = [&](int col) {
+    for (int g = 0; g < 2; ++g) {
+      const int seg = g == 0 ? p.ep.b_seg : p.ep.a_seg;
+      if (seg >= 0 && col >= p.ep.seg_off[seg] && col < p.ep.seg_off[seg + 1]) return true;
+    }
+    return false;
+  };
+  int lo = 0;
+  while (lo < p.N) {
+    const bool g = gated(lo);
+    int hi = p.N;
+    for (int i = 0; i < ncut; ++i)  // next cut where the gate state may change
+      if (cuts[i] > lo && gated(cuts[i] < p.N ? cuts[i] : p.N - 1) != g) {
+        hi = cuts[i];
+        break;
+      }
+    const hipError_t e = launch_range(p, lo, hi, g, s);
+    if (e != hipSuccess) return e;
+    lo = hi;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nvfp4

@@ -244,13 +244,18 @@ def dequantize_segments(w_codes, w_scales, seg_offsets, seg_g, cols: int) -> np.
     return np.concatenate(parts, axis=0)
 
 
-def fused_segments(a_codes, a_scales, a_g, w_codes, w_scales, seg_offsets, seg_g, cols: int):
+def fused_segments(a_codes, a_scales, a_g, w_codes, w_scales, seg_offsets, seg_g, cols: int,
+                   with_tol: bool = True):
     """Fused multi-module GEMM: column n of the output uses the global scale
     of the segment that holds weight row n.  Equal, by definition, to the
-    concatenation of one GEMM per segment.  Returns (ref, tol)."""
+    concatenation of one GEMM per segment.  Returns (ref, tol); tol is None
+    when with_tol is False."""
     va = dequantize(a_codes, a_scales, a_g, cols)
     vw = dequantize_segments(w_codes, w_scales, seg_offsets, seg_g, cols)
-    return va @ vw.T, GEMM_REL_TOL * (np.abs(va) @ np.abs(vw).T)
+    ref = va @ vw.T
+    if not with_tol:
+        return ref, None
+    return ref, GEMM_REL_TOL * (np.abs(va) @ np.abs(vw).T)
 
 
 # ---------------------------------------------------------------------------
