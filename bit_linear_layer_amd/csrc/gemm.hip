@@ -33,6 +33,12 @@
 
 #include "internal.h"
 
+// The LLVM intrinsic behind buffer_load ... lds (LDS DMA), declared by name.
+typedef int32_t nvfp4_i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(
+    nvfp4_i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
+    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 namespace nvfp4 {
 
 namespace {
@@ -46,10 +52,14 @@ constexpr int kBK = 128;              // K elements per tile
 constexpr int kRowCodeBytes = kBK / 2;  // 64 code bytes per row per tile
 constexpr int kRowScaleBytes = kBK / 16;  // 8 scale bytes per row per tile
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+// SCHED_VALU > 0: after each k-step's MFMAs, ask the scheduler to interleave
+// them one by one with SCHED_VALU decode VALU ops (measured per config).
+template <int BM_, int BN_, int WGM_, int WGN_, int SCHED_VALU>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int kSchedValu = SCHED_VALU;
   static constexpr int kThreads = WGM * WGN * 64;
+  static constexpr int kWavesPerSimd = kThreads / 256;  // one workgroup per CU
   static constexpr int TM = BM / WGM, TN = BN / WGN;  // wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;    // 32x32 fragments per wave
   static constexpr int kACode = BM * kRowCodeBytes;
@@ -110,72 +120,120 @@ __device__ inline float sigmoidf_(float x) {
 }
 __device__ inline float softplusf_(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
 
-// Stage one K tile of A and W into registers.  Row pointers (rows beyond
-// M or N clamped to the last row: their results are never stored) and LDS
-// destinations are computed once; a K tile advances them by 64 code bytes
-// and 8 scale bytes.  Only the last, partial K tile takes the masked path.
+// Asynchronous global -> LDS copy of one full K tile with gfx950's
+// buffer_load ... lds (LDS DMA): no VGPR staging, no ds_write.  One
+// instruction moves one 1 KB "group" = 64 lanes x 16 bytes, written to
+// LDS at (group base + lane * 16); the group layout above makes lane l of
+// fragment f, parity c, fetch 16 code bytes of row 32f + l%32 at chunk
+// q = 2(l/32) + c.  Scale groups move 64 lanes x 4 bytes the same way.
+// Waves split the groups round-robin.  Row offsets beyond M/N are clamped
+// to the last row (results of those rows are never stored).  The K tile
+// index enters as the uniform soffset, so the per-lane offsets are fixed.
+typedef nvfp4_i32x4 i32x4;
+typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
+
+
+__device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)((uint32_t)(a >> 32) & 0xFFFFu);  // stride 0: raw byte buffer
+  r[2] = (int32_t)bytes;                             // num_records (bytes)
+  r[3] = 0x00020000;                                 // gfx9 buffer format word
+  return r;
+}
+
 template <class C>
-struct TileLoader {
-  u32x4 chunk[C::kChunkIters];
-  uint2 sc[C::kScaleIters];
-  const uint8_t* cptr[C::kChunkIters];
-  const uint8_t* sptr[C::kScaleIters];
-  int cdst[C::kChunkIters];
-  int sdst[C::kScaleIters];
+struct AsyncLoader {
+  static constexpr int kWaves = C::kThreads / 64;
+  static constexpr int kCodeGroups = (C::BM + C::BN) / 32 * 2;
+  static constexpr int kScaleGroups = (C::BM + C::BN) / 32;
+  static constexpr int kCodePer = (kCodeGroups + kWaves - 1) / kWaves;
+  static constexpr int kScalePer = (kScaleGroups + kWaves - 1) / kWaves;
+  i32x4 ra_c, ra_s, rw_c, rw_s;
+  int cvoff[kCodePer], svoff[kScalePer];
+  int clds[kCodePer], slds[kScalePer];  // wave-uniform LDS offsets in the stage
+  bool cB[kCodePer], sB[kScalePer];
 
-  __device__ void init(const GemmArgs& p, int m0, int n0, int n_hi) {
+  __device__ void init(const GemmArgs& p, int m0, int n0, int n_hi, int wave, int lane) {
+    ra_c = buffer_rsrc(p.a_codes, (uint32_t)((int64_t)p.M * p.lda_c));
+    ra_s = buffer_rsrc(p.a_scales, (uint32_t)((int64_t)p.M * p.lda_s));
+    rw_c = buffer_rsrc(p.w_codes, (uint32_t)((int64_t)n_hi * p.ldw_c));
+    rw_s = buffer_rsrc(p.w_scales, (uint32_t)((int64_t)n_hi * p.ldw_s));
 #pragma unroll
-    for (int it = 0; it < C::kChunkIters; ++it) {
-      const int id = it * C::kThreads + (int)threadIdx.x;
-      const int cid = id < C::kChunks ? id : 0;
-      const bool isB = cid >= C::BM * 4;
-      const int lid = isB ? cid - C::BM * 4 : cid;
-      const int row = lid >> 2, q = lid & 3;
+    for (int i = 0; i < kCodePer; ++i) {
+      int g = wave + i * kWaves;
+      if (g >= kCodeGroups) g = 0;  // idle slot (never issued)
+      const bool isB = g >= C::BM / 32 * 2;
+      const int gg = isB ? g - C::BM / 32 * 2 : g;
+      const int f = gg >> 1, c = gg & 1;
+      const int row = f * 32 + (lane & 31), q = 2 * (lane >> 5) + c;
       const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
-      cptr[it] = (isB ? p.w_codes + (int64_t)grow * p.ldw_c : p.a_codes + (int64_t)grow * p.lda_c) + q * 16;
-      cdst[it] = (isB ? C::kACode : 0) + code_slot(row, q);
+      cvoff[i] = (int)(grow * (isB ? p.ldw_c : p.lda_c)) + q * 16;
+      clds[i] = (isB ? C::kACode : 0) + f * 2048 + c * 1024;
+      cB[i] = isB;
     }
 #pragma unroll
-    for (int it = 0; it < C::kScaleIters; ++it) {
-      const int id = it * C::kThreads + (int)threadIdx.x;
-      const int sid = id < C::BM + C::BN ? id : 0;
-      const bool isB = sid >= C::BM;
-      const int row = isB ? sid - C::BM : sid;
+    for (int i = 0; i < kScalePer; ++i) {
+      int g = wave + i * kWaves;
+      if (g >= kScaleGroups) g = 0;
+      const bool isB = g >= C::BM / 32;
+      const int f = isB ? g - C::BM / 32 : g;
+      const int row = f * 32 + (lane & 31), h = lane >> 5;
       const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
-      sptr[it] = isB ? p.w_scales + (int64_t)grow * p.ldw_s : p.a_scales + (int64_t)grow * p.lda_s;
-      sdst[it] = C::kACode + C::kBCode + (isB ? C::kAScale : 0) + scale_slot(row, 0);
+      svoff[i] = (int)(grow * (isB ? p.ldw_s : p.lda_s)) + h * 4;
+      slds[i] = C::kACode + C::kBCode + (isB ? C::kAScale : 0) + f * 256;
+      sB[i] = isB;
     }
   }
 
-  __device__ static bool active_chunk(int it) {
-    return C::kChunks % C::kThreads == 0 || it * C::kThreads + (int)threadIdx.x < C::kChunks;
-  }
-  __device__ static bool active_scale(int it) {
-    return (C::BM + C::BN) % C::kThreads == 0 || it * C::kThreads + (int)threadIdx.x < C::BM + C::BN;
-  }
-
-  // A full K tile (k0 + 128 <= K): unmasked vector loads.
-  __device__ void load_full(int kt) {
+  // Every wave issues exactly kCodePer + kScalePer copies per tile (idle
+  // slots repeat group 0: identical bytes to identical LDS addresses), so
+  // a fixed vmcnt tells how many tiles are still in flight.
+  static constexpr int kPerTile = kCodePer + kScalePer;
+  __device__ void issue(uint8_t* stage, int kt) const {
 #pragma unroll
-    for (int it = 0; it < C::kChunkIters; ++it)
-      if (active_chunk(it)) chunk[it] = *reinterpret_cast<const u32x4*>(cptr[it] + kt * kRowCodeBytes);
+    for (int i = 0; i < kCodePer; ++i)
+      llvm_amdgcn_raw_buffer_load_lds(cB[i] ? rw_c : ra_c, (lds_u32_ptr)(stage + clds[i]), 16, cvoff[i],
+                                      kt * kRowCodeBytes, 0, 0);
 #pragma unroll
-    for (int it = 0; it < C::kScaleIters; ++it)
-      if (active_scale(it)) sc[it] = *reinterpret_cast<const uint2*>(sptr[it] + kt * kRowScaleBytes);
+    for (int i = 0; i < kScalePer; ++i)
+      llvm_amdgcn_raw_buffer_load_lds(sB[i] ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[i]), 4, svoff[i],
+                                      kt * kRowScaleBytes, 0, 0);
   }
+};
 
-  // The last K tile when K % 128 != 0: zero everything beyond K (a zero
-  // code and a zero scale byte both decode to 0).
-  __device__ void load_tail(const GemmArgs& p, int kt) {
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// The last K tile when K % 128 != 0, through registers: everything beyond K
+// is zero (a zero code and a zero scale byte both decode to 0).
+template <class C>
+struct TailLoader {
+  static constexpr int kChunkIters = (C::kChunks + C::kThreads - 1) / C::kThreads;
+  static constexpr int kScaleIters = (C::BM + C::BN + C::kThreads - 1) / C::kThreads;
+  u32x4 chunk[kChunkIters];
+  uint2 sc[kScaleIters];
+
+  __device__ void load(const GemmArgs& p, int m0, int n0, int n_hi, int kt) {
     const int k0 = kt * kBK;
 #pragma unroll
-    for (int it = 0; it < C::kChunkIters; ++it) {
+    for (int it = 0; it < kChunkIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (active_chunk(it)) {
-        const int id = it * C::kThreads + (int)threadIdx.x;
-        const int q = id & 3;  // chunk ids of A and B both start at multiples of 4
+      if (id < C::kChunks) {
+        const bool isB = id >= C::BM * 4;
+        const int lid = isB ? id - C::BM * 4 : id;
+        const int row = lid >> 2, q = lid & 3;
+        const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+        const uint8_t* src = (isB ? p.w_codes + (int64_t)grow * p.ldw_c : p.a_codes + (int64_t)grow * p.lda_c) +
+                             (k0 >> 1) + q * 16;
         const int rem = p.K - (k0 + q * 32);
-        const uint8_t* src = cptr[it] + kt * kRowCodeBytes;
         if (rem >= 32) {
           v = *reinterpret_cast<const u32x4*>(src);
         } else if (rem > 0) {  // rem == 16: the first 8 bytes only
@@ -188,10 +246,15 @@ struct TileLoader {
     }
     const int nb = (p.K >> 4) - kt * kRowScaleBytes;  // valid scale bytes in this tile (1..7)
 #pragma unroll
-    for (int it = 0; it < C::kScaleIters; ++it) {
+    for (int it = 0; it < kScaleIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
       uint32_t lo = 0, hi = 0;
-      if (active_scale(it)) {
-        const uint8_t* src = sptr[it] + kt * kRowScaleBytes;
+      if (id < C::BM + C::BN) {
+        const bool isB = id >= C::BM;
+        const int row = isB ? id - C::BM : id;
+        const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+        const uint8_t* src = (isB ? p.w_scales + (int64_t)grow * p.ldw_s : p.a_scales + (int64_t)grow * p.lda_s) +
+                             kt * kRowScaleBytes;
         for (int b = 0; b < nb; ++b) {
           const uint32_t byte = src[b];
           if (b < 4) lo |= byte << (8 * b);
@@ -202,21 +265,27 @@ struct TileLoader {
     }
   }
 
-  __device__ void load(const GemmArgs& p, int kt) {
-    if ((kt + 1) * kBK <= p.K) load_full(kt);
-    else load_tail(p, kt);
-  }
-
   __device__ void store(uint8_t* stage) const {
 #pragma unroll
-    for (int it = 0; it < C::kChunkIters; ++it)
-      if (active_chunk(it)) *reinterpret_cast<u32x4*>(stage + cdst[it]) = chunk[it];
-#pragma unroll
-    for (int it = 0; it < C::kScaleIters; ++it)
-      if (active_scale(it)) {
-        *reinterpret_cast<uint32_t*>(stage + sdst[it]) = sc[it].x;
-        *reinterpret_cast<uint32_t*>(stage + sdst[it] + 128) = sc[it].y;  // h = 1: 32 lanes on
+    for (int it = 0; it < kChunkIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
+      if (id < C::kChunks) {
+        const bool isB = id >= C::BM * 4;
+        const int lid = isB ? id - C::BM * 4 : id;
+        *reinterpret_cast<u32x4*>(stage + (isB ? C::kACode : 0) + code_slot(lid >> 2, lid & 3)) = chunk[it];
       }
+    }
+#pragma unroll
+    for (int it = 0; it < kScaleIters; ++it) {
+      const int id = it * C::kThreads + (int)threadIdx.x;
+      if (id < C::BM + C::BN) {
+        const bool isB = id >= C::BM;
+        const int row = isB ? id - C::BM : id;
+        uint8_t* reg = stage + C::kACode + C::kBCode + (isB ? C::kAScale : 0);
+        *reinterpret_cast<uint32_t*>(reg + scale_slot(row, 0)) = sc[it].x;
+        *reinterpret_cast<uint32_t*>(reg + scale_slot(row, 1)) = sc[it].y;
+      }
+    }
   }
 };
 
@@ -242,7 +311,7 @@ __device__ inline void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, i
 // instantiation with the gate epilogue; the host launches it only over the
 // gate segments' columns, so the bulk of the output runs gate-free code.
 template <class C, bool GATE>
-__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kWavesPerSimd, C::kWavesPerSimd)))
 void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
@@ -252,7 +321,7 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   const int m0 = tm * C::BM, n0 = n_lo + tn * C::BN;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int fm0 = wm * C::FM, fn0 = wn * C::FN;  // first fragment (of 32 rows/cols) in the tile
 
@@ -264,21 +333,15 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (p.K + kBK - 1) / kBK;
-  TileLoader<C> ld;
-  ld.init(p, m0, n0, n_hi);
-  ld.load(p, 0);
-  ld.store(smem);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) ld.load(p, kt + 1);
-    const uint8_t* st = smem + (kt & 1) * C::kStage;
+  // One K tile from LDS stage `st`: this wave's fragments (32 code bytes +
+  // 4 scale bytes per lane each), then 8 k-steps in which the decode of
+  // step t+1 overlaps the MFMAs of step t.  `prefetch` runs right after the
+  // LDS reads (it issues the next tile's copy into the other stage).
+  auto compute_tile = [&](const uint8_t* st, auto prefetch) {
     const uint8_t* sA = st;
     const uint8_t* sB = st + C::kACode;
     const uint8_t* sAs = st + C::kACode + C::kBCode;
     const uint8_t* sBs = sAs + C::kAScale;
-
     u32x4 ac[C::FM][2], bc[C::FN][2];
     uint32_t as[C::FM], bs[C::FN];
 #pragma unroll
@@ -293,32 +356,85 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
       bc[j][1] = *reinterpret_cast<const u32x4*>(sB + (fn0 + j) * 2048 + 1024 + lane * 16);
       bs[j] = *reinterpret_cast<const uint32_t*>(sBs + (fn0 + j) * 256 + lane * 4);
     }
+    prefetch();
 
+    half2v sa2[C::FM], sb2[C::FN];
+    half8 a_cur[C::FM], b_cur[C::FN];
 #pragma unroll
-    for (int t2 = 0; t2 < 4; ++t2) {  // pairs of k-steps share one scale byte
-      half2v sa2[C::FM], sb2[C::FN];
+    for (int i = 0; i < C::FM; ++i) sa2[i] = scale_pair(as[i], 0);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) sa2[i] = scale_pair(as[i], t2);
+    for (int j = 0; j < C::FN; ++j) sb2[j] = scale_pair(bs[j], 0);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) sb2[j] = scale_pair(bs[j], t2);
+    for (int i = 0; i < C::FM; ++i) a_cur[i] = decode8(ac[i][0][0], sa2[i]);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = 2 * t2 + u;
-        half8 a[C::FM], b[C::FN];
+    for (int j = 0; j < C::FN; ++j) b_cur[j] = decode8(bc[j][0][0], sb2[j]);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = decode8(ac[i][t >> 2][t & 3], sa2[i]);
+    for (int t = 0; t < 8; ++t) {
+      half8 a_nxt[C::FM], b_nxt[C::FN];
+      if (t < 7) {
+        const int u = t + 1;
+        if ((u & 1) == 0) {  // k-steps 2v and 2v+1 share scale byte v
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = decode8(bc[j][t >> 2][t & 3], sb2[j]);
+          for (int i = 0; i < C::FM; ++i) sa2[i] = scale_pair(as[i], u >> 1);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+          for (int j = 0; j < C::FN; ++j) sb2[j] = scale_pair(bs[j], u >> 1);
+        }
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < C::FM; ++i) a_nxt[i] = decode8(ac[i][u >> 2][u & 3], sa2[i]);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) b_nxt[j] = decode8(bc[j][u >> 2][u & 3], sb2[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[i], b_cur[j], acc[i][j], 0, 0, 0);
+      if (t < 7) {
+        if constexpr (C::kSchedValu > 0) {
+          // interleave: one MFMA, then kSchedValu decode VALU ops, repeated
+#pragma unroll
+          for (int g = 0; g < C::FM * C::FN; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, C::kSchedValu, 0);   // VALU
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) a_cur[i] = a_nxt[i];
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) b_cur[j] = b_nxt[j];
       }
     }
+  };
 
-    if (kt + 1 < nk) ld.store(smem + ((kt + 1) & 1) * C::kStage);
+  // Three LDS stages: tile kt computes while tiles kt+1 and kt+2 stream in.
+  constexpr int kStages = 3;
+  constexpr int kPer = AsyncLoader<C>::kPerTile;
+  const int nk_full = p.K / kBK;  // full K tiles: asynchronous LDS-DMA path
+  AsyncLoader<C> ld;
+  ld.init(p, m0, n0, n_hi, wave, lane);
+  if (nk_full > 0) ld.issue(smem, 0);
+  if (nk_full > 1) {
+    ld.issue(smem + C::kStage, 1);
+    wait_vmem<kPer>();  // tile 0 landed, tile 1 may still fly
+  } else {
+    wait_vmem<0>();
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk_full; ++kt) {
+    compute_tile(smem + (kt % kStages) * C::kStage, [&] {
+      if (kt + 2 < nk_full) ld.issue(smem + ((kt + 2) % kStages) * C::kStage, kt + 2);
+    });
+    if (kt + 2 < nk_full) wait_vmem<kPer>();  // tile kt+1 landed
+    else wait_vmem<0>();
     __syncthreads();
+  }
+  if (p.K % kBK != 0) {  // partial last K tile through registers, zero-filled beyond K
+    uint8_t* st = smem + (nk_full % kStages) * C::kStage;
+    TailLoader<C> tl;
+    tl.load(p, m0, n0, n_hi, nk_full);
+    tl.store(st);
+    __syncthreads();
+    compute_tile(st, [] {});
   }
 
   // Epilogue: per output column its segment's global scale (and gate).
@@ -390,7 +506,7 @@ hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
   const int tiles_n = (n_hi - n_lo + C::BN - 1) / C::BN;
   const int64_t nblocks = (int64_t)tiles_m * tiles_n;
-  const size_t lds = 2 * (size_t)C::kStage;
+  const size_t lds = 3 * (size_t)C::kStage;  // three stages
   // raising the dynamic-LDS limit is idempotent and cheap
   hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C, GATE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -399,9 +515,12 @@ hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   return hipGetLastError();
 }
 
-using CfgL = TileCfg<256, 256, 2, 2>;  // large prefill shapes
-using CfgM = TileCfg<128, 128, 2, 2>;  // medium shapes / better wave fill
-using CfgS = TileCfg<32, 128, 1, 4>;   // M <= 32
+// Large prefill shapes: 8 waves, two per SIMD, so one wave's decode VALU
+// work runs while the other's MFMAs occupy the matrix core (measured: one
+// wave per SIMD barely overlaps its own decode with its MFMAs).
+using CfgL = TileCfg<256, 256, 4, 2, 7>;
+using CfgM = TileCfg<128, 128, 2, 2, 0>;  // medium shapes / better wave fill
+using CfgS = TileCfg<32, 128, 1, 4, 0>;   // M <= 32
 
 double fill(int64_t tiles) {
   const int64_t waves = (tiles + 255) / 256;
