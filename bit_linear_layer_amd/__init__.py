@@ -136,10 +136,10 @@ class NVFP4Tensor:
 
 
 def empty_nvfp4(rows: int, cols: int, device="cuda") -> NVFP4Tensor:
-    """Allocate an NVFP4 matrix with the row strides the kernels require
-    (codes rows on 16-byte, scale rows on 8-byte boundaries)."""
+    """Allocate an NVFP4 matrix with the row strides the kernels want: code
+    and scale rows on 16-byte boundaries."""
     ldc = _round_up(max(cols // 2, 1), 16)
-    lds = _round_up(max(cols // 16, 1), 8)
+    lds = _round_up(max(cols // 16, 1), 16)  # 16-byte rows also suit the decode path's copies
     codes = torch.empty((rows, ldc), dtype=torch.uint8, device=device)
     scales = torch.empty((rows, lds), dtype=torch.uint8, device=device)
     g = torch.empty(1, dtype=torch.float32, device=device)

@@ -1,0 +1,91 @@
+// Device helpers shared by the NVFP4 GEMM kernels: exact decode of E2M1
+// codes times an E4M3 block scale into fp16, bf16 rounding, gate functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// The LLVM intrinsic behind buffer_load ... lds (LDS DMA), declared by name.
+typedef int32_t nvfp4_i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(
+    nvfp4_i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
+    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+namespace nvfp4 {
+namespace dev {
+
+typedef nvfp4_i32x4 i32x4;
+typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
+
+
+__device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)((uint32_t)(a >> 32) & 0xFFFFu);  // stride 0: raw byte buffer
+  r[2] = (int32_t)bytes;                             // num_records (bytes)
+  r[3] = 0x00020000;                                 // gfx9 buffer format word
+  return r;
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// E4M3 byte -> fp16 pair (s, s), exact: the byte shifted into an fp16's
+// exponent/mantissa fields is s * 2^-8 (normal and subnormal alike).
+__device__ inline half2v scale_pair(uint32_t sdw, int idx) {
+  const uint32_t b = (sdw >> (8 * idx)) & 0xFFu;
+  const uint32_t bits = (b << 7) | (b << 23);
+  half2v h = __builtin_bit_cast(half2v, bits);
+  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  return h * k256;
+}
+
+// 8 E2M1 codes (one dword) times their block scale -> 8 exact fp16 values.
+__device__ inline half8 decode8(uint32_t codes, half2v s2) {
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+  p0 *= s2;
+  p1 *= s2;
+  p2 *= s2;
+  p3 *= s2;
+  half8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// GDN gate epilogue on one scaled fp32 accumulator x (chatpaper.ai English
+// abstract, mechanism (ii): sigmoid write strength, log-space
+// softplus/exponential decay).  kind 1: sigmoid(x); kind 2:
+// -exp_alog * softplus(x + dtb) with exp_alog = exp(A_log[h]); else x.
+// One exp and one log1p: sigmoid(t) = 1/(1+e^-t), softplus(t) =
+// max(t,0) + log1p(e^-|t|).
+__device__ inline float gate_value(float x, int kind, float exp_alog, float dtb) {
+  const float t = kind == 2 ? x + dtb : x;
+  const float e = expf(-fabsf(t));
+  const float sig = (t >= 0.0f ? 1.0f : e) / (1.0f + e);
+  const float dec = -exp_alog * (fmaxf(t, 0.0f) + log1pf(e));
+  return kind == 1 ? sig : (kind == 2 ? dec : x);
+}
+
+}  // namespace dev
+}  // namespace nvfp4

@@ -31,22 +31,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_util.h"
 #include "internal.h"
-
-// The LLVM intrinsic behind buffer_load ... lds (LDS DMA), declared by name.
-typedef int32_t nvfp4_i32x4 __attribute__((ext_vector_type(4)));
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(
-    nvfp4_i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
-    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 namespace nvfp4 {
 
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace dev;
 
 constexpr int kBK = 128;              // K elements per tile
 constexpr int kRowCodeBytes = kBK / 2;  // 64 code bytes per row per tile
@@ -83,43 +75,6 @@ __device__ inline int scale_slot(int row, int h) {
   return (row >> 5) * 256 + ((((h) << 5) | (row & 31)) << 2);
 }
 
-// E4M3 byte -> fp16 pair (s, s), exact: the byte shifted into an fp16's
-// exponent/mantissa fields is s * 2^-8 (normal and subnormal alike).
-__device__ inline half2v scale_pair(uint32_t sdw, int idx) {
-  const uint32_t b = (sdw >> (8 * idx)) & 0xFFu;
-  const uint32_t bits = (b << 7) | (b << 23);
-  half2v h = __builtin_bit_cast(half2v, bits);
-  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
-  return h * k256;
-}
-
-// 8 E2M1 codes (one dword) times their block scale -> 8 exact fp16 values.
-__device__ inline half8 decode8(uint32_t codes, half2v s2) {
-  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
-  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
-  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
-  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
-  p0 *= s2;
-  p1 *= s2;
-  p2 *= s2;
-  p3 *= s2;
-  half8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ inline float sigmoidf_(float x) {
-  const float e = expf(-fabsf(x));
-  return x >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
-}
-__device__ inline float softplusf_(float z) { return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z))); }
-
 // Asynchronous global -> LDS copy of one full K tile with gfx950's
 // buffer_load ... lds (LDS DMA): no VGPR staging, no ds_write.  One
 // instruction moves one 1 KB "group" = 64 lanes x 16 bytes, written to
@@ -129,20 +84,6 @@ __device__ inline float softplusf_(float z) { return fmaxf(z, 0.0f) + log1pf(exp
 // Waves split the groups round-robin.  Row offsets beyond M/N are clamped
 // to the last row (results of those rows are never stored).  The K tile
 // index enters as the uniform soffset, so the per-lane offsets are fixed.
-typedef nvfp4_i32x4 i32x4;
-typedef __attribute__((address_space(3))) uint32_t* lds_u32_ptr;
-
-
-__device__ inline i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = (int32_t)(uint32_t)a;
-  r[1] = (int32_t)((uint32_t)(a >> 32) & 0xFFFFu);  // stride 0: raw byte buffer
-  r[2] = (int32_t)bytes;                             // num_records (bytes)
-  r[3] = 0x00020000;                                 // gfx9 buffer format word
-  return r;
-}
-
 template <class C>
 struct AsyncLoader {
   static constexpr int kWaves = C::kThreads / 64;
@@ -202,14 +143,6 @@ struct AsyncLoader {
                                       kt * kRowScaleBytes, 0, 0);
   }
 };
-
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14,
-// expcnt and lgkmcnt left at "no wait").
-template <int N>
-__device__ inline void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // The last K tile when K % 128 != 0, through registers: everything beyond K
 // is zero (a zero code and a zero scale byte both decode to 0).
@@ -468,13 +401,7 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
       for (int r = 0; r < 16; ++r) {
         const float x = acc[i][j][r] * colscale[j];
         if constexpr (GATE) {
-          // one exp and one log1p per element: sigmoid(x) = 1/(1+e^-x),
-          // softplus(z) = max(z,0) + log1p(e^-|z|), with t = x or z
-          const float t = kind[j] == 2 ? x + dtb[j] : x;
-          const float e = expf(-fabsf(t));
-          const float sig = (t >= 0.0f ? 1.0f : e) / (1.0f + e);
-          const float dec = -alog[j] * (fmaxf(t, 0.0f) + log1pf(e));
-          acc[i][j][r] = kind[j] == 1 ? sig : (kind[j] == 2 ? dec : x);
+          acc[i][j][r] = gate_value(x, kind[j], alog[j], dtb[j]);
         } else {
           acc[i][j][r] = x;
         }
@@ -529,6 +456,7 @@ double fill(int64_t tiles) {
 
 hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s) {
   const int n = n_hi - n_lo;
+  if (skinny_eligible(p)) return launch_gemm_skinny(p, n_lo, n_hi, gate, s);
   if (gate) {
     if (p.M <= 32) return launch_cfg<CfgS, true>(p, n_lo, n_hi, s);
     return launch_cfg<CfgM, true>(p, n_lo, n_hi, s);

@@ -56,4 +56,8 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t s);
 
+// Small-M (decode) path over the columns [n_lo, n_hi) when skinny_eligible().
+bool skinny_eligible(const GemmArgs& p);
+hipError_t launch_gemm_skinny(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s);
+
 }  // namespace nvfp4

@@ -202,3 +202,38 @@ def test_decode_full_size():
     wc, ws, sg = oracle_weight(wq, offs, seg_g)
     ref, tol = O.fused_segments(ac, as_, ag, wc, ws, offs, sg, 5120)
     assert_close(out, ref, tol, "bf16", "decode")
+
+
+# ------------------------------------------------- small-M (decode) path
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 16), (3, 40, 48), (8, 1000, 144), (16, 257, 1040),
+                                   (5, 4099, 5120), (8, 700, 5104), (2, 96, 5136), (16, 2048, 4096)],
+                         ids=lambda v: str(v))
+def test_small_m_shapes(m, n, k):
+    """M <= 16 runs the weight-streaming kernel (K <= 5120) or the tiled
+    kernel beyond; ragged N, K % 128 != 0 and K % 32 == 16 included."""
+    say(f"small-M gemm {m}x{n}x{k}")
+    x = rand_bf16(m * 101 + k, m, k, outliers=min(2, k // 16))
+    w = rand_bf16(n * 7 + k, n, k, 0.02)
+    out, ref, tol = run_gemm(x, w, torch.float32)
+    assert_close(out, ref, tol, "f32")
+
+
+def test_small_m_fused_segments_with_gates():
+    say("small-M fused GDN with gates")
+    wl, x, wq, offs, seg_g = small_gdn(m=4)
+    a = quantize_dev(x)
+    gate = dict(b_segment=4, a_segment=5, A_log=wl.extra["A_log"].to(DEV), dt_bias=wl.extra["dt_bias"].to(DEV))
+    out = nv.gemm_fused_segments(a, wq, offs, seg_g, gate=gate, out_dtype=torch.float32)
+    ac, as_, ag = host_q(a)
+    wc, ws, sg = oracle_weight(wq, offs, seg_g)
+    ref, tol = O.fused_segments(ac, as_, ag, wc, ws, offs, sg, x.shape[1])
+    lin = slice(0, offs[4])
+    assert_close(out[:, lin], ref[:, lin], tol[:, lin], "f32", "linear")
+    a_log = wl.extra["A_log"].numpy().astype(np.float64)
+    dt_bias = wl.extra["dt_bias"].numpy().astype(np.float64)
+    bsl, asl = slice(offs[4], offs[5]), slice(offs[5], offs[6])
+    beta, tb, _, _ = O.gate_tolerances(ref[:, bsl], tol[:, bsl], a_log, dt_bias)
+    _, _, dec, td = O.gate_tolerances(ref[:, asl], tol[:, asl], a_log, dt_bias)
+    assert_close(out[:, bsl], beta, tb, "f32", "sigmoid gate")
+    assert_close(out[:, asl], dec, td, "f32", "decay gate")
