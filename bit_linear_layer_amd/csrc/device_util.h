@@ -37,6 +37,15 @@ __device__ inline void wait_vmem() {
 }
 
 
+// Workgroup barrier for kernels that count their own LDS-DMA copies with
+// wait_vmem: it waits for this wave's LDS reads and writes only.  (A
+// __syncthreads() also drains every vector-memory operation in flight, copies
+// meant to land a few iterations later included.)  The "memory" clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ inline void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -66,6 +75,24 @@ __device__ inline half8 decode8(uint32_t codes, half2v s2) {
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
   r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
   return r;
+}
+
+// Map the linear workgroup id to an output tile.  Workgroups are dealt to
+// the 8 XCDs round-robin; renumber them so each XCD works on a contiguous
+// range of tiles (sharing its L2), then walk that range in column-major
+// groups of kGroupM tile rows so neighbours share A and W panels.
+__device__ inline void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcd = 8, kGroupM = 8;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  const int x = bid % kXcd, slot = bid / kXcd;
+  const int l = x * q + min(x, r) + slot;
+  const int group_size = kGroupM * tiles_n;
+  const int group = l / group_size;
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in = l - group * group_size;
+  tm = first_m + in % gm;
+  tn = in / gm;
 }
 
 __device__ inline uint32_t f32_to_bf16_bits(float f) {

@@ -16,12 +16,13 @@
 // rounds.  The global scales are applied once, in the epilogue.
 //
 // Data path per workgroup (BM x BN output tile, BK = 128):
-//   global -> registers -> LDS, raw packed codes + scale bytes (0.5625 B per
-//   element, 3.6x less LDS traffic than staging fp16), double-buffered;
-//   each wave reads its fragments from LDS in MFMA lane order (one 16-byte
-//   read per lane, consecutive lanes consecutive addresses) and decodes them
-//   in registers: 4 x v_cvt_scalef32_pk_f16_fp4 + 4 x v_pk_mul_f16 per
-//   8 elements; then v_mfma_f32_32x32x16_f16.
+//   global -> LDS by LDS-DMA (buffer_load ... lds, no VGPR staging), raw
+//   packed codes + scale bytes (0.5625 B per element, 3.6x less LDS traffic
+//   than staging fp16), three stages so two tiles are in flight while one is
+//   computed; each wave reads its fragments from LDS in MFMA lane order (one
+//   16-byte read per lane, consecutive lanes consecutive addresses) and
+//   decodes them in registers: 4 x v_cvt_scalef32_pk_f16_fp4 + 4 x
+//   v_pk_mul_f16 per 8 elements; then v_mfma_f32_32x32x16_f16.
 //
 // K order inside a 128-wide K tile.  The MFMA sums over its 16 k values, so
 // any permutation of k that A and W share is allowed.  Lane (row, h) of a
@@ -222,24 +223,6 @@ struct TailLoader {
   }
 };
 
-// Map the linear workgroup id to an output tile.  Workgroups are dealt to
-// the 8 XCDs round-robin; renumber them so each XCD works on a contiguous
-// range of tiles (sharing its L2), then walk that range in column-major
-// groups of kGroupM tile rows so neighbours share A and W panels.
-__device__ inline void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int kXcd = 8, kGroupM = 8;
-  const int q = nblocks / kXcd, r = nblocks % kXcd;
-  const int x = bid % kXcd, slot = bid / kXcd;
-  const int l = x * q + min(x, r) + slot;
-  const int group_size = kGroupM * tiles_n;
-  const int group = l / group_size;
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int in = l - group * group_size;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
-
 // One launch covers the output columns [n_lo, n_hi).  GATE selects the
 // instantiation with the gate epilogue; the host launches it only over the
 // gate segments' columns, so the bulk of the output runs gate-free code.
@@ -352,21 +335,21 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   } else {
     wait_vmem<0>();
   }
-  __syncthreads();
+  barrier_lds();
   for (int kt = 0; kt < nk_full; ++kt) {
     compute_tile(smem + (kt % kStages) * C::kStage, [&] {
       if (kt + 2 < nk_full) ld.issue(smem + ((kt + 2) % kStages) * C::kStage, kt + 2);
     });
     if (kt + 2 < nk_full) wait_vmem<kPer>();  // tile kt+1 landed
     else wait_vmem<0>();
-    __syncthreads();
+    barrier_lds();
   }
   if (p.K % kBK != 0) {  // partial last K tile through registers, zero-filled beyond K
     uint8_t* st = smem + (nk_full % kStages) * C::kStage;
     TailLoader<C> tl;
     tl.load(p, m0, n0, n_hi, nk_full);
     tl.store(st);
-    __syncthreads();
+    barrier_lds();
     compute_tile(st, [] {});
   }
 
