@@ -3,16 +3,17 @@
 
 One step = one pass of the whole path over the 8192-token MLP pair: dynamic
 NVFP4 quantization of X [8192, 5120] -> fused gate|up GEMM (two segments,
-each with its own global scale) -> SiLU*mul (+ amax partials) ->
-quantization of h [8192, 17408] -> down GEMM.  Every step runs in the
+each with its own global scale) with SiLU*mul and the amax partials of h in
+its epilogue -> quantization of h [8192, 17408] -> down GEMM.  Every step runs in the
 library's HIP kernels on torch's current stream; inputs are synthetic,
 seeded and resident in HBM before the timed region.
 
 Prints ONE JSON line: TFLOP/s including activation quantization (algorithmic
 2*M*N*K of both GEMMs over the time of every stage), the roofline of the
-dominant kernel (the gate|up GEMM, timed live with HIP events on the launch
-stream), the decode-shape (M=8) weight-streaming GB/s, and the CPU oracle
-timed on a bounded sample of the same workload.
+dominant kernel (the gate|up GEMM with the SiLU*mul epilogue, timed live
+with HIP events on the launch stream), the decode-shape (M=8)
+weight-streaming GB/s, and the CPU oracle timed on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode / GDN measurements")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration) and exit")
     return ap.parse_args()
@@ -120,7 +121,6 @@ def main():
     w_d, d_offs, d_g = quant_segments([wl.extra["w_down"]])
     a = nv.empty_nvfp4(m, k, dev)
     hq = nv.empty_nvfp4(m, inter, dev)
-    gu = torch.empty((m, 2 * inter), dtype=torch.bfloat16, device=dev)
     h = torch.empty((m, inter), dtype=torch.bfloat16, device=dev)
     out = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
     ws_x = nv.workspace_for(m, k, dev)
@@ -131,10 +131,9 @@ def main():
         nv.nvfp4_quantize(x, a, nv.SCALE_DYNAMIC, ws_x)
         if ev is not None:
             ev[0].record(stream)
-        nv.nvfp4_gemm_fused_segments(a, w_gu, gu_offs, gu_g, gu)
+        nv.nvfp4_gemm_swiglu(a, w_gu, gu_g, h=h, amax_workspace=ws_h)
         if ev is not None:
             ev[1].record(stream)
-        nv.nvfp4_silu_mul(gu, h, inter, ws_h)
         nv.nvfp4_quantize(h, hq, nv.AMAX_PRECOMPUTED, ws_h)
         nv.nvfp4_gemm_fused_segments(hq, w_d, d_offs, d_g, out)
 
@@ -164,7 +163,7 @@ def main():
     gu_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     achieved = flops_gu / (gu_ms * 1e-3) / 1e12
     traffic = read_traffic()
-    roofline = {"bound": "mfma", "kernel": "nvfp4 gemm (gate|up, 8192x34816x5120)",
+    roofline = {"bound": "mfma", "kernel": "nvfp4 gemm + swiglu epilogue (gate|up, 8192x34816x5120)",
                 "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
                 "avg_launch_ms": round(gu_ms, 4)}
@@ -177,7 +176,8 @@ def main():
         "dtype": "nvfp4 (e2m1+e4m3) -> f16 mfma, f32 accumulate",
         "data": "synthetic (seeded; random-init weights)",
         "config": {"workload": wl.name, "M": m, "K": k, "inter": inter,
-                   "gate_up": [2 * inter, k], "down": [k, inter], "parallelism": "single-gpu"},
+                   "gate_up": [2 * inter, k], "down": [k, inter], "glue": "silu*mul + amax in gate|up epilogue",
+                   "parallelism": "single-gpu"},
         "pct_of_mfma_peak": round(100.0 * value / MFMA_F16_PEAK_TFLOPS, 2),
         "roofline": roofline,
     }
@@ -185,12 +185,60 @@ def main():
     # --------------------------------------------- decode shape (M = 8)
     if not args.no_secondary:
         result["secondary"] = secondary(nv, W, torch, np, dev, stream, log)
+        result["secondary"].update(mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g,
+                                                w_d, d_offs, d_g, hq, h, out, ws_x, ws_h, flops))
 
     # --------------------------------------------------- CPU oracle leg
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(nv, W, torch, np, wl, a, w_gu, gu_offs, gu_g, w_d, d_offs, d_g,
                                               args.cpu_rows, log)
     print(json.dumps(result), flush=True)
+
+
+def time_steps(torch, stream, fn, steps=10, warmup=3):
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g, w_d, d_offs, d_g, hq, h, out,
+                 ws_x, ws_h, flops):
+    """The same MLP pair step two other ways: unfused glue (bf16 gate|up
+    tensor, SiLU*mul kernel), and h quantized in the gate|up epilogue with a
+    static (calibrated) global scale, here h's dynamic scale from one
+    untimed pass, standing in for a checkpoint's calibrated value."""
+    m, inter = h.shape
+    gu = torch.empty((m, 2 * inter), dtype=torch.bfloat16, device=dev)
+
+    def unfused():
+        nv.nvfp4_quantize(x, a, nv.SCALE_DYNAMIC, ws_x)
+        nv.nvfp4_gemm_fused_segments(a, w_gu, gu_offs, gu_g, gu)
+        nv.nvfp4_silu_mul(gu, h, inter, ws_h)
+        nv.nvfp4_quantize(h, hq, nv.AMAX_PRECOMPUTED, ws_h)
+        nv.nvfp4_gemm_fused_segments(hq, w_d, d_offs, d_g, out)
+
+    hs = nv.empty_nvfp4(m, inter, dev)
+    unfused()
+    hs.global_scale.copy_(hq.global_scale)  # calibration pass (untimed)
+
+    def static_h():
+        nv.nvfp4_quantize(x, a, nv.SCALE_DYNAMIC, ws_x)
+        nv.nvfp4_gemm_swiglu(a, w_gu, gu_g, h_q=hs)
+        nv.nvfp4_gemm_fused_segments(hs, w_d, d_offs, d_g, out)
+
+    res = {}
+    for name, fn in (("mlp_pair_unfused_glue", unfused), ("mlp_pair_static_h_scale", static_h)):
+        ms = time_steps(torch, stream, fn)
+        res[name] = {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        log(f"{name}: {ms:.3f} ms/step = {res[name]['tflops']} TFLOP/s")
+    return res
 
 
 def secondary(nv, W, torch, np, dev, stream, log):

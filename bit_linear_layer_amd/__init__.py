@@ -73,6 +73,9 @@ def load() -> ctypes.CDLL:
         lib.nvfp4_gemm_fused_segments.restype = ctypes.c_int
         lib.nvfp4_silu_mul.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _P, ctypes.c_size_t, _P]
         lib.nvfp4_silu_mul.restype = ctypes.c_int
+        lib.nvfp4_gemm_swiglu.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), _P, _P, _I64,
+                                          _P, ctypes.c_size_t, ctypes.POINTER(_Tensor), _P]
+        lib.nvfp4_gemm_swiglu.restype = ctypes.c_int
         lib.nvfp4_status_string.argtypes = [ctypes.c_int]
         lib.nvfp4_status_string.restype = ctypes.c_char_p
         lib.nvfp4_version.argtypes = []
@@ -203,6 +206,22 @@ def nvfp4_silu_mul(gu: torch.Tensor, h: torch.Tensor, inter: int, amax_workspace
     _check(st, "nvfp4_silu_mul")
 
 
+def nvfp4_gemm_swiglu(a: NVFP4Tensor, w_gate_up: NVFP4Tensor, seg_global_scales: torch.Tensor,
+                      h: torch.Tensor | None = None, amax_workspace: torch.Tensor | None = None,
+                      h_q: NVFP4Tensor | None = None, stream=None) -> None:
+    """C ``nvfp4_gemm_swiglu``: h = bf16(silu(gate) * up) from one GEMM over
+    w_gate_up = [gate; up] (2 segments), written as bf16 ``h`` and/or as
+    NVFP4 ``h_q`` quantized with the static scale already in h_q.global_scale."""
+    ws_bytes = 0 if amax_workspace is None else amax_workspace.numel() * amax_workspace.element_size()
+    da, dw = a.descriptor(), w_gate_up.descriptor()
+    dq = None if h_q is None else h_q.descriptor()
+    st = load().nvfp4_gemm_swiglu(
+        ctypes.byref(da), ctypes.byref(dw), seg_global_scales.data_ptr(), _ptr(h),
+        0 if h is None else h.stride(0), _ptr(amax_workspace), ws_bytes,
+        None if dq is None else ctypes.byref(dq), _stream(a.codes.device, stream))
+    _check(st, "nvfp4_gemm_swiglu")
+
+
 # ----------------------------------------------------------- conveniences
 
 def quantize(x: torch.Tensor, static_scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -237,3 +256,23 @@ def silu_mul(gu: torch.Tensor, amax_workspace: torch.Tensor | None = None, out: 
     h = out if out is not None else torch.empty((gu.shape[0], inter), dtype=torch.bfloat16, device=gu.device)
     nvfp4_silu_mul(gu, h, inter, amax_workspace)
     return h
+
+
+def gemm_swiglu(a: NVFP4Tensor, w_gate_up: NVFP4Tensor, seg_global_scales: torch.Tensor,
+                amax_workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 h [M, inter] of the fused gate_up GEMM + SiLU*mul."""
+    inter = w_gate_up.rows // 2
+    h = out if out is not None else torch.empty((a.rows, inter), dtype=torch.bfloat16, device=a.codes.device)
+    nvfp4_gemm_swiglu(a, w_gate_up, seg_global_scales, h=h, amax_workspace=amax_workspace)
+    return h
+
+
+def gemm_swiglu_quantized(a: NVFP4Tensor, w_gate_up: NVFP4Tensor, seg_global_scales: torch.Tensor,
+                          static_scale: torch.Tensor, out: NVFP4Tensor | None = None) -> NVFP4Tensor:
+    """NVFP4 h [M, inter] with the calibrated global scale ``static_scale``
+    (device float32 [1]), straight from the fused gate_up epilogue."""
+    inter = w_gate_up.rows // 2
+    q = out if out is not None else empty_nvfp4(a.rows, inter, a.codes.device)
+    q.global_scale.copy_(static_scale)
+    nvfp4_gemm_swiglu(a, w_gate_up, seg_global_scales, h_q=q)
+    return q

@@ -145,6 +145,70 @@ int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* w, void* out, int out_
                                    ld_out, stream);
 }
 
+int nvfp4_gemm_swiglu(const nvfp4_tensor* a, const nvfp4_tensor* w_gate_up,
+                      const float* seg_global_scales, void* h, int64_t ld_h,
+                      void* amax_workspace, size_t workspace_bytes, const nvfp4_tensor* h_q,
+                      void* stream) {
+  int st = check_tensor(a);
+  if (st != NVFP4_OK) return st;
+  st = check_tensor(w_gate_up);
+  if (st != NVFP4_OK) return st;
+  if (a->global_scale == nullptr || seg_global_scales == nullptr) return NVFP4_ERR_NULL;
+  if (h == nullptr && h_q == nullptr) return NVFP4_ERR_NULL;
+  if (a->cols != w_gate_up->cols || w_gate_up->rows % 2 != 0) return NVFP4_ERR_SHAPE;
+  const int64_t inter = w_gate_up->rows / 2;
+  if (inter % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (h != nullptr) {
+    if (ld_h < inter || ld_h % 8 != 0) return NVFP4_ERR_STRIDE;
+    if (!aligned(h, 16)) return NVFP4_ERR_ALIGN;
+  }
+  if (h_q != nullptr) {
+    st = check_tensor(h_q);
+    if (st != NVFP4_OK) return st;
+    if (h_q->global_scale == nullptr) return NVFP4_ERR_NULL;
+    if (h_q->rows != a->rows || h_q->cols != inter) return NVFP4_ERR_SHAPE;
+  }
+  const int np = partial_count(a->rows, inter, 16);
+  if (amax_workspace != nullptr) {
+    if (workspace_bytes < sizeof(float) * (size_t)np) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(amax_workspace, 4)) return NVFP4_ERR_ALIGN;
+  }
+
+  GemmArgs p{};
+  p.a_codes = a->codes;
+  p.a_scales = a->scales;
+  p.lda_c = a->ld_codes;
+  p.lda_s = a->ld_scales;
+  p.w_codes = w_gate_up->codes;
+  p.w_scales = w_gate_up->scales;
+  p.ldw_c = w_gate_up->ld_codes;
+  p.ldw_s = w_gate_up->ld_scales;
+  p.M = (int)a->rows;
+  p.N = (int)w_gate_up->rows;
+  p.K = (int)a->cols;
+  p.ep.n_seg = 2;
+  p.ep.seg_off[0] = 0;
+  p.ep.seg_off[1] = (int)inter;
+  p.ep.seg_off[2] = (int)(2 * inter);
+  p.ep.seg_g = seg_global_scales;
+  p.ep.a_g = a->global_scale;
+  p.ep.b_seg = -1;
+  p.ep.a_seg = -1;
+  p.ep.inter = (int)inter;
+  p.ep.h = (uint16_t*)h;
+  p.ep.ld_h = ld_h;
+  if (h_q != nullptr) {
+    p.ep.hq_codes = const_cast<uint8_t*>(h_q->codes);  // an output here
+    p.ep.hq_scales = const_cast<uint8_t*>(h_q->scales);
+    p.ep.hq_ld_codes = h_q->ld_codes;
+    p.ep.hq_ld_scales = h_q->ld_scales;
+    p.ep.hq_g = h_q->global_scale;
+  }
+  p.ep.partials = (float*)amax_workspace;
+  p.ep.n_partials = np;
+  return hip_status(launch_gemm_swiglu(p, (hipStream_t)stream));
+}
+
 int nvfp4_silu_mul(const void* gu, int64_t rows, int64_t inter, int64_t ld_gu, void* h,
                    int64_t ld_h, void* amax_workspace, size_t workspace_bytes, void* stream) {
   if (gu == nullptr || h == nullptr) return NVFP4_ERR_NULL;

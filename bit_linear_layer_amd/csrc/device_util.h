@@ -95,9 +95,27 @@ __device__ inline void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, i
   tn = in / gm;
 }
 
+// float -> bf16 bits, round to nearest even (finite inputs).
 __device__ inline uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// silu(u) = u * sigmoid(u), with sigmoid evaluated without overflow.  The
+// SiLU*mul kernel and the fused gate_up epilogue both call this one
+// definition, so their bf16 results agree bit for bit.
+__device__ inline float silu(float u) {
+  const float e = expf(-fabsf(u));
+  const float sig = u >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
+  return u * sig;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
 }
 
 // GDN gate epilogue on one scaled fp32 accumulator x (chatpaper.ai English

@@ -34,6 +34,7 @@
 
 #include "device_util.h"
 #include "internal.h"
+#include "quant_block.h"
 
 namespace nvfp4 {
 
@@ -76,6 +77,32 @@ __device__ inline int scale_slot(int row, int h) {
   return (row >> 5) * 256 + ((((h) << 5) | (row & 31)) << 2);
 }
 
+// Epilogue modes.  kEpiGate: GDN gate columns.  kEpiSwiglu: the tile's 256
+// W rows are 128 gate rows and the 128 matching up rows (see w_row), and the
+// epilogue writes h = silu(gate) * up for 128 columns of h.
+enum { kEpiPlain = 0, kEpiGate = 1, kEpiSwiglu = 2 };
+
+// Output columns covered by one tile.
+template <class C, int EPI>
+constexpr int tile_cols() { return EPI == kEpiSwiglu ? C::BN / 2 : C::BN; }
+
+// Weight row feeding tile-local B row `row` (0..BN-1), clamped in range.
+// kEpiSwiglu: wave column wn owns fragments FN*wn .. FN*wn+FN-1; its first
+// FN/2 fragments hold gate rows and the others the up rows of the same h
+// columns, so each lane ends with gate and up accumulators side by side.
+template <class C, int EPI>
+__device__ inline int w_row(const GemmArgs& p, int n0, int n_hi, int row) {
+  if constexpr (EPI == kEpiSwiglu) {
+    constexpr int TN = C::BN / C::WGN;
+    const int f = row >> 5, wn = f / C::FN, j = f % C::FN;
+    const bool up = j >= C::FN / 2;
+    const int hl = wn * (TN / 2) + (up ? j - C::FN / 2 : j) * 32 + (row & 31);
+    return (up ? p.ep.inter : 0) + min(n0 + hl, p.ep.inter - 1);
+  } else {
+    return min(n0 + row, n_hi - 1);
+  }
+}
+
 // Asynchronous global -> LDS copy of one full K tile with gfx950's
 // buffer_load ... lds (LDS DMA): no VGPR staging, no ds_write.  One
 // instruction moves one 1 KB "group" = 64 lanes x 16 bytes, written to
@@ -85,7 +112,7 @@ __device__ inline int scale_slot(int row, int h) {
 // Waves split the groups round-robin.  Row offsets beyond M/N are clamped
 // to the last row (results of those rows are never stored).  The K tile
 // index enters as the uniform soffset, so the per-lane offsets are fixed.
-template <class C>
+template <class C, int EPI>
 struct AsyncLoader {
   static constexpr int kWaves = C::kThreads / 64;
   static constexpr int kCodeGroups = (C::BM + C::BN) / 32 * 2;
@@ -100,8 +127,8 @@ struct AsyncLoader {
   __device__ void init(const GemmArgs& p, int m0, int n0, int n_hi, int wave, int lane) {
     ra_c = buffer_rsrc(p.a_codes, (uint32_t)((int64_t)p.M * p.lda_c));
     ra_s = buffer_rsrc(p.a_scales, (uint32_t)((int64_t)p.M * p.lda_s));
-    rw_c = buffer_rsrc(p.w_codes, (uint32_t)((int64_t)n_hi * p.ldw_c));
-    rw_s = buffer_rsrc(p.w_scales, (uint32_t)((int64_t)n_hi * p.ldw_s));
+    rw_c = buffer_rsrc(p.w_codes, (uint32_t)((int64_t)p.N * p.ldw_c));
+    rw_s = buffer_rsrc(p.w_scales, (uint32_t)((int64_t)p.N * p.ldw_s));
 #pragma unroll
     for (int i = 0; i < kCodePer; ++i) {
       int g = wave + i * kWaves;
@@ -110,7 +137,7 @@ struct AsyncLoader {
       const int gg = isB ? g - C::BM / 32 * 2 : g;
       const int f = gg >> 1, c = gg & 1;
       const int row = f * 32 + (lane & 31), q = 2 * (lane >> 5) + c;
-      const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+      const int grow = isB ? w_row<C, EPI>(p, n0, n_hi, row) : min(m0 + row, p.M - 1);
       cvoff[i] = (int)(grow * (isB ? p.ldw_c : p.lda_c)) + q * 16;
       clds[i] = (isB ? C::kACode : 0) + f * 2048 + c * 1024;
       cB[i] = isB;
@@ -122,7 +149,7 @@ struct AsyncLoader {
       const bool isB = g >= C::BM / 32;
       const int f = isB ? g - C::BM / 32 : g;
       const int row = f * 32 + (lane & 31), h = lane >> 5;
-      const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+      const int grow = isB ? w_row<C, EPI>(p, n0, n_hi, row) : min(m0 + row, p.M - 1);
       svoff[i] = (int)(grow * (isB ? p.ldw_s : p.lda_s)) + h * 4;
       slds[i] = C::kACode + C::kBCode + (isB ? C::kAScale : 0) + f * 256;
       sB[i] = isB;
@@ -147,7 +174,7 @@ struct AsyncLoader {
 
 // The last K tile when K % 128 != 0, through registers: everything beyond K
 // is zero (a zero code and a zero scale byte both decode to 0).
-template <class C>
+template <class C, int EPI>
 struct TailLoader {
   static constexpr int kChunkIters = (C::kChunks + C::kThreads - 1) / C::kThreads;
   static constexpr int kScaleIters = (C::BM + C::BN + C::kThreads - 1) / C::kThreads;
@@ -164,7 +191,7 @@ struct TailLoader {
         const bool isB = id >= C::BM * 4;
         const int lid = isB ? id - C::BM * 4 : id;
         const int row = lid >> 2, q = lid & 3;
-        const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+        const int grow = isB ? w_row<C, EPI>(p, n0, n_hi, row) : min(m0 + row, p.M - 1);
         const uint8_t* src = (isB ? p.w_codes + (int64_t)grow * p.ldw_c : p.a_codes + (int64_t)grow * p.lda_c) +
                              (k0 >> 1) + q * 16;
         const int rem = p.K - (k0 + q * 32);
@@ -186,7 +213,7 @@ struct TailLoader {
       if (id < C::BM + C::BN) {
         const bool isB = id >= C::BM;
         const int row = isB ? id - C::BM : id;
-        const int grow = isB ? min(n0 + row, n_hi - 1) : min(m0 + row, p.M - 1);
+        const int grow = isB ? w_row<C, EPI>(p, n0, n_hi, row) : min(m0 + row, p.M - 1);
         const uint8_t* src = (isB ? p.w_scales + (int64_t)grow * p.ldw_s : p.a_scales + (int64_t)grow * p.lda_s) +
                              kt * kRowScaleBytes;
         for (int b = 0; b < nb; ++b) {
@@ -223,18 +250,95 @@ struct TailLoader {
   }
 };
 
-// One launch covers the output columns [n_lo, n_hi).  GATE selects the
-// instantiation with the gate epilogue; the host launches it only over the
-// gate segments' columns, so the bulk of the output runs gate-free code.
-template <class C, bool GATE>
+// Gated-MLP epilogue.  Lane (row, h column) holds the gate accumulator in
+// fragment j and the up accumulator in fragment j + FN/2.  Each is scaled and
+// rounded to bf16 exactly as the plain epilogue stores it, then
+// h = bf16(silu(gate) * up) as the SiLU*mul kernel computes it, so h is bit
+// for bit the unfused chain's.  Outputs: bf16 h, the amax of |h| (one
+// atomic max per wave into partials[workgroup % n]), and/or h quantized
+// with a static global scale: h is staged in LDS as bf16 [BM][BN/2] and
+// each thread quantizes whole 16-element blocks of a row from there.
+template <class C>
+__device__ __attribute__((always_inline)) inline void swiglu_epilogue(
+    const GemmArgs& p, floatx16 (&acc)[C::FM][C::FN], int m0, int n0, int fm0, int wn, int lane,
+    uint8_t* smem) {
+  static_assert(C::FN % 2 == 0, "gate and up fragments pair up");
+  constexpr int FH = C::FN / 2;
+  constexpr int TH = C::BN / C::WGN / 2;  // h columns per wave
+  constexpr int kHCols = C::BN / 2;       // h columns per tile
+  const float ga = *p.ep.a_g;
+  const float sg = ga * p.ep.seg_g[0], su = ga * p.ep.seg_g[1];
+  const bool quant = p.ep.hq_codes != nullptr;
+  uint16_t* th = reinterpret_cast<uint16_t*>(smem);  // [BM][kHCols] bf16 h
+  if (quant) barrier_lds();  // every wave is done reading the last K tile
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int ml = (fm0 + i) * 32 + 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < FH; ++j) {
+      const int hl = wn * TH + j * 32 + (lane & 31);
+      const int hcol = n0 + hl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int mloc = ml + 8 * (r >> 2) + (r & 3);
+        const int m = m0 + mloc;
+        const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][r] * sg));
+        const float u = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + FH][r] * su));
+        const uint32_t hb = f32_to_bf16_bits(silu(g) * u);
+        if (m < p.M && hcol < p.ep.inter) {
+          amax = fmaxf(amax, __uint_as_float((hb & 0x7FFFu) << 16));
+          if (p.ep.h != nullptr) p.ep.h[(int64_t)m * p.ep.ld_h + hcol] = (uint16_t)hb;
+        }
+        if (quant) th[mloc * kHCols + hl] = (uint16_t)hb;
+      }
+    }
+  }
+  if (p.ep.partials != nullptr) {
+    amax = wave_max(amax);  // |h| >= 0: float order is unsigned integer order
+    if (lane == 0)
+      atomicMax(reinterpret_cast<unsigned int*>(p.ep.partials) + blockIdx.x % p.ep.n_partials,
+                __float_as_uint(amax));
+  }
+  if (quant) {
+    barrier_lds();
+    const float gh = *p.ep.hq_g;
+    constexpr int kBlocksPerRow = kHCols / 16;
+    for (int b = (int)threadIdx.x; b < C::BM * kBlocksPerRow; b += C::kThreads) {
+      const int mloc = b / kBlocksPerRow, jb = b % kBlocksPerRow;
+      const int m = m0 + mloc, h0 = n0 + jb * 16;
+      if (m >= p.M || h0 >= p.ep.inter) continue;  // inter % 16 == 0: blocks are whole
+      const uint16_t* src = th + mloc * kHCols + jb * 16;
+      const uint4 q0 = *reinterpret_cast<const uint4*>(src);
+      const uint4 q1 = *reinterpret_cast<const uint4*>(src + 8);
+      const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      float v[16];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+      uint2 c;
+      const uint32_t sc = quantize_block16(v, gh, &c);
+      *reinterpret_cast<uint2*>(p.ep.hq_codes + (int64_t)m * p.ep.hq_ld_codes + h0 / 2) = c;
+      p.ep.hq_scales[(int64_t)m * p.ep.hq_ld_scales + h0 / 16] = (uint8_t)sc;
+    }
+  }
+}
+
+// One launch covers the output columns [n_lo, n_hi).  EPI = kEpiGate is
+// launched only over the gate segments' columns, so the bulk of the output
+// runs gate-free code; kEpiSwiglu covers the columns of h.
+template <class C, int EPI>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kWavesPerSimd, C::kWavesPerSimd)))
 void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
-  const int tiles_n = (n_hi - n_lo + C::BN - 1) / C::BN;
+  constexpr int kCols = tile_cols<C, EPI>();
+  const int tiles_n = (n_hi - n_lo + kCols - 1) / kCols;
   int tm, tn;
   tile_of((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * C::BM, n0 = n_lo + tn * C::BN;
+  const int m0 = tm * C::BM, n0 = n_lo + tn * kCols;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -324,9 +428,9 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
 
   // Three LDS stages: tile kt computes while tiles kt+1 and kt+2 stream in.
   constexpr int kStages = 3;
-  constexpr int kPer = AsyncLoader<C>::kPerTile;
+  constexpr int kPer = AsyncLoader<C, EPI>::kPerTile;
   const int nk_full = p.K / kBK;  // full K tiles: asynchronous LDS-DMA path
-  AsyncLoader<C> ld;
+  AsyncLoader<C, EPI> ld;
   ld.init(p, m0, n0, n_hi, wave, lane);
   if (nk_full > 0) ld.issue(smem, 0);
   if (nk_full > 1) {
@@ -346,11 +450,16 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   }
   if (p.K % kBK != 0) {  // partial last K tile through registers, zero-filled beyond K
     uint8_t* st = smem + (nk_full % kStages) * C::kStage;
-    TailLoader<C> tl;
+    TailLoader<C, EPI> tl;
     tl.load(p, m0, n0, n_hi, nk_full);
     tl.store(st);
     barrier_lds();
     compute_tile(st, [] {});
+  }
+
+  if constexpr (EPI == kEpiSwiglu) {
+    swiglu_epilogue<C>(p, acc, m0, n0, fm0, wn, lane, smem);
+    return;
   }
 
   // Epilogue: per output column its segment's global scale (and gate).
@@ -367,7 +476,7 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
     kind[j] = 0;
     alog[j] = 0.0f;
     dtb[j] = 0.0f;
-    if constexpr (GATE) {
+    if constexpr (EPI == kEpiGate) {
       kind[j] = (seg == p.ep.b_seg) ? 1 : (seg == p.ep.a_seg ? 2 : 0);
       if (kind[j] == 2 && n < n_hi) {
         const int h = n - p.ep.seg_off[seg];
@@ -383,7 +492,7 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float x = acc[i][j][r] * colscale[j];
-        if constexpr (GATE) {
+        if constexpr (EPI == kEpiGate) {
           acc[i][j][r] = gate_value(x, kind[j], alog[j], dtb[j]);
         } else {
           acc[i][j][r] = x;
@@ -411,17 +520,18 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   }
 }
 
-template <class C, bool GATE>
+template <class C, int EPI>
 hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
-  const int tiles_n = (n_hi - n_lo + C::BN - 1) / C::BN;
+  constexpr int kCols = tile_cols<C, EPI>();
+  const int tiles_n = (n_hi - n_lo + kCols - 1) / kCols;
   const int64_t nblocks = (int64_t)tiles_m * tiles_n;
   const size_t lds = 3 * (size_t)C::kStage;  // three stages
   // raising the dynamic-LDS limit is idempotent and cheap
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C, GATE>,
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C, EPI>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  gemm_kernel<C, GATE><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p, n_lo, n_hi);
+  gemm_kernel<C, EPI><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p, n_lo, n_hi);
   return hipGetLastError();
 }
 
@@ -441,14 +551,14 @@ hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStr
   const int n = n_hi - n_lo;
   if (skinny_eligible(p)) return launch_gemm_skinny(p, n_lo, n_hi, gate, s);
   if (gate) {
-    if (p.M <= 32) return launch_cfg<CfgS, true>(p, n_lo, n_hi, s);
-    return launch_cfg<CfgM, true>(p, n_lo, n_hi, s);
+    if (p.M <= 32) return launch_cfg<CfgS, kEpiGate>(p, n_lo, n_hi, s);
+    return launch_cfg<CfgM, kEpiGate>(p, n_lo, n_hi, s);
   }
-  if (p.M <= 32) return launch_cfg<CfgS, false>(p, n_lo, n_hi, s);
+  if (p.M <= 32) return launch_cfg<CfgS, kEpiPlain>(p, n_lo, n_hi, s);
   const int64_t tl = (int64_t)((p.M + 255) / 256) * ((n + 255) / 256);
   const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((n + 127) / 128);
-  if (p.M >= 256 && n >= 256 && fill(tl) >= 0.8 * fill(tmd)) return launch_cfg<CfgL, false>(p, n_lo, n_hi, s);
-  return launch_cfg<CfgM, false>(p, n_lo, n_hi, s);
+  if (p.M >= 256 && n >= 256 && fill(tl) >= 0.8 * fill(tmd)) return launch_cfg<CfgL, kEpiPlain>(p, n_lo, n_hi, s);
+  return launch_cfg<CfgM, kEpiPlain>(p, n_lo, n_hi, s);
 }
 
 }  // namespace
@@ -493,6 +603,19 @@ hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {
     lo = hi;
   }
   return hipSuccess;
+}
+
+hipError_t launch_gemm_swiglu(const GemmArgs& p, hipStream_t s) {
+  if (p.ep.partials != nullptr) {
+    const hipError_t e = launch_zero(p.ep.partials, p.ep.n_partials, s);
+    if (e != hipSuccess) return e;
+  }
+  const int inter = p.ep.inter;
+  const int64_t tl = (int64_t)((p.M + 255) / 256) * ((inter + 127) / 128);
+  const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((inter + 63) / 64);
+  if (p.M >= 256 && inter >= 128 && fill(tl) >= 0.8 * fill(tmd))
+    return launch_cfg<CfgL, kEpiSwiglu>(p, 0, inter, s);
+  return launch_cfg<CfgM, kEpiSwiglu>(p, 0, inter, s);
 }
 
 }  // namespace nvfp4

@@ -6,29 +6,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_util.h"
 #include "internal.h"
 
 namespace nvfp4 {
 
 namespace {
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-
-__device__ inline uint32_t bf16_rne_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs only
-}
-
-// silu(u) = u * sigmoid(u), with sigmoid evaluated without overflow.
-__device__ inline float silu(float u) {
-  const float e = expf(-fabsf(u));
-  const float sig = u >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
-  return u * sig;
-}
+using namespace dev;
 
 __global__ __launch_bounds__(kElemThreads) void silu_mul_kernel(
     const uint16_t* __restrict__ gu, int64_t ld_gu, uint16_t* __restrict__ h, int64_t ld_h,
@@ -55,7 +40,7 @@ __global__ __launch_bounds__(kElemThreads) void silu_mul_kernel(
     for (int i = 0; i < 4; ++i) {
       const float h0 = silu(__uint_as_float(gw[i] << 16)) * __uint_as_float(uw[i] << 16);
       const float h1 = silu(__uint_as_float(gw[i] & 0xFFFF0000u)) * __uint_as_float(uw[i] & 0xFFFF0000u);
-      const uint32_t b0 = bf16_rne_bits(h0), b1 = bf16_rne_bits(h1);
+      const uint32_t b0 = f32_to_bf16_bits(h0), b1 = f32_to_bf16_bits(h1);
       hw[i] = b0 | (b1 << 16);
       m = fmaxf(m, fmaxf(__uint_as_float((b0 & 0x7FFFu) << 16), __uint_as_float((b1 & 0x7FFFu) << 16)));
     }
@@ -74,7 +59,17 @@ __global__ __launch_bounds__(kElemThreads) void silu_mul_kernel(
   }
 }
 
+__global__ __launch_bounds__(kElemThreads) void zero_kernel(float* __restrict__ p, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0.0f;
+}
+
 }  // namespace
+
+hipError_t launch_zero(float* p, int n, hipStream_t s) {
+  zero_kernel<<<(n + kElemThreads - 1) / kElemThreads, kElemThreads, 0, s>>>(p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_silu_mul(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
                            uint16_t* h, int64_t ld_h, float* partials, int n_partials,

@@ -38,6 +38,17 @@ struct EpilogueArgs {
   int b_seg, a_seg;                     // gate segments, -1 = none
   const float* A_log;
   const float* dt_bias;
+  // Gated-MLP epilogue (launch_gemm_swiglu): W rows [0, inter) are the gate,
+  // [inter, 2 inter) the up projection; h = bf16(silu(gate) * up).
+  int inter;
+  uint16_t* h;                 // bf16 [M, inter] or null
+  int64_t ld_h;
+  uint8_t* hq_codes;           // NVFP4 h with the static global scale *hq_g, or null
+  uint8_t* hq_scales;
+  int64_t hq_ld_codes, hq_ld_scales;
+  const float* hq_g;
+  float* partials;             // amax partials of h (atomic max, zeroed first) or null
+  int n_partials;
 };
 
 struct GemmArgs {
@@ -55,6 +66,11 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t s);
+
+// Gated-MLP first half in one launch (zeroes ep.partials first when set).
+hipError_t launch_gemm_swiglu(const GemmArgs& args, hipStream_t s);
+
+hipError_t launch_zero(float* p, int n, hipStream_t s);
 
 // Small-M (decode) path over the columns [n_lo, n_hi) when skinny_eligible().
 bool skinny_eligible(const GemmArgs& p);

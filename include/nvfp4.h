@@ -176,6 +176,43 @@ int nvfp4_gemm_fused_segments(const nvfp4_tensor* a, const nvfp4_tensor* w, int 
 int nvfp4_silu_mul(const void* gu, int64_t rows, int64_t inter, int64_t ld_gu, void* h,
                    int64_t ld_h, void* amax_workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * nvfp4_gemm_swiglu -- the first half of a gated MLP in one launch: the
+ * gate_up GEMM of nvfp4_gemm_fused_segments with two segments (gate, up),
+ * followed in the same kernel by nvfp4_silu_mul's arithmetic.  The pages
+ * fix no MLP detail; the gate|up row layout is this library's reading.
+ * The static-scale output serves the per-module calibrated checkpoints the
+ * pages describe (chatpaper.ai English abstract: per-module-calibrated NVFP4
+ * checkpoints served by fused kernels).  The results are bit for bit those
+ * of nvfp4_gemm_fused_segments (bf16 out) + nvfp4_silu_mul + nvfp4_quantize,
+ * without the bf16 gate_up tensor (and, with h_q, without h) in memory.
+ *
+ *   a                  activations, [M, K].
+ *   w_gate_up          weight, [2*inter, K]: rows [0, inter) are the gate
+ *                      projection, rows [inter, 2*inter) the up projection.
+ *   seg_global_scales  DEVICE float32 [2]: the gate's and the up
+ *                      projection's global scales.
+ *   h, ld_h            DEVICE bf16 [M, inter] output with ld_h (elements,
+ *                      >= inter, multiple of 8), 16-byte aligned; or NULL.
+ *   amax_workspace     NULL, or >= nvfp4_quantize_workspace_bytes(M, inter)
+ *                      bytes of device memory (4-byte aligned) receiving the
+ *                      amax partials of h, as nvfp4_silu_mul writes them: a
+ *                      following nvfp4_quantize of h with
+ *                      NVFP4_AMAX_PRECOMPUTED and this workspace computes
+ *                      h's dynamic global scale without an amax pass.
+ *   h_q                NULL, or an NVFP4 output [M, inter] whose
+ *                      global_scale (device) holds a calibrated scale; its
+ *                      codes and scales are written as nvfp4_quantize(h,
+ *                      NVFP4_SCALE_STATIC) would write them.
+ * At least one of h and h_q; inter % 16 == 0; w_gate_up->rows == 2*inter.
+ * Errors as nvfp4_gemm_fused_segments, plus NVFP4_ERR_WORKSPACE for a short
+ * workspace.
+ */
+int nvfp4_gemm_swiglu(const nvfp4_tensor* a, const nvfp4_tensor* w_gate_up,
+                      const float* seg_global_scales, void* h, int64_t ld_h,
+                      void* amax_workspace, size_t workspace_bytes, const nvfp4_tensor* h_q,
+                      void* stream);
+
 /* Human-readable text of a status (and of the last HIP error, for NVFP4_ERR_HIP). */
 const char* nvfp4_status_string(int status);
 

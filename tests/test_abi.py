@@ -113,3 +113,23 @@ def test_silu_mul_rejects_bad_arguments():
     assert f(FAKE + 4, 4, 16, 32, FAKE, 16, None, 0, None) == -5
     assert f(FAKE, 4, 16, 32, FAKE, 16, FAKE, 0, None) == -8
     assert f(FAKE, 4, 8, 16, FAKE, 8, FAKE, 4096, None) == -2  # amax partials need inter % 16 == 0
+
+
+def swiglu(a=None, w=None, sg=FAKE, h=FAKE, ldh=16, ws=None, wsb=0, hq=None):
+    a = a or tensor()
+    w = w or tensor(rows=32)  # inter = 16
+    return nv.load().nvfp4_gemm_swiglu(ctypes.byref(a), ctypes.byref(w), sg, h, ldh, ws, wsb,
+                                       None if hq is None else ctypes.byref(hq), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sg=None), -1), (dict(h=None), -1), (dict(a=tensor(g=0)), -1),
+    (dict(w=tensor(rows=31)), -2), (dict(w=tensor(rows=24)), -2),  # odd rows; inter % 16 != 0
+    (dict(w=tensor(rows=32, cols=48, ldc=32)), -2),
+    (dict(ldh=8), -4), (dict(ldh=20), -4), (dict(h=FAKE + 2), -5),
+    (dict(ws=FAKE, wsb=0), -8),
+    (dict(h=None, hq=tensor(rows=4, cols=32, g=0)), -1), (dict(h=None, hq=tensor(rows=5, cols=16)), -2),
+    (dict(h=None, hq=tensor(rows=4, cols=16, ldc=4)), -4),
+])
+def test_swiglu_rejects_bad_arguments(kw, status):
+    assert swiglu(**kw) == status
