@@ -185,6 +185,7 @@ def main():
     # --------------------------------------------- decode shape (M = 8)
     if not args.no_secondary:
         result["secondary"] = secondary(nv, W, torch, np, dev, stream, log)
+        result["secondary"].update(kv_fp8(nv, W, torch, dev, stream, log))
         result["secondary"].update(mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g,
                                                 w_d, d_offs, d_g, hq, h, out, ws_x, ws_h, flops))
 
@@ -239,6 +240,42 @@ def mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g, w_d, d_
         res[name] = {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
         log(f"{name}: {ms:.3f} ms/step = {res[name]['tflops']} TFLOP/s")
     return res
+
+
+def kv_fp8(nv, W, torch, dev, stream, log):
+    """FP8 KV-cache write and read of one layer's K tensor [32768, 1024]
+    (bf16), four rotating input/cache pairs (> the 256 MB MALL), with the
+    calibrated scale and with the unit (uncalibrated) scale."""
+    wl = W.kv_cache()
+    xs = [wl.x.to(dev)] + [wl.x.to(dev).mul_(1.0 + 0.001 * i) for i in range(1, 4)]
+    rows, cols = xs[0].shape
+    caches = [torch.empty((rows, cols), dtype=torch.uint8, device=dev) for _ in range(4)]
+    outs = [torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    s_cal = nv.kv_fp8_calibrate(xs[0])
+    s_one = torch.ones(1, dtype=torch.float32, device=dev)
+    ws = nv.workspace_for(rows, cols, dev)
+    n = rows * cols
+    res = {}
+
+    def rate(name, fn, nbytes):
+        ms = time_steps(torch, stream, fn, steps=40, warmup=4)  # fn itself rotates buffers
+        res[name] = {"us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    it = [0]
+
+    def nxt():
+        it[0] += 1
+        return it[0] % 4
+
+    rate("kv_fp8_write_calibrated", lambda: (lambda i: nv.nvfp4_kv_fp8_quantize(xs[i], caches[i], s_cal))(nxt()), 3 * n)
+    rate("kv_fp8_write_unit_scale", lambda: (lambda i: nv.nvfp4_kv_fp8_quantize(xs[i], caches[i], s_one))(nxt()), 3 * n)
+    rate("kv_fp8_read_bf16", lambda: (lambda i: nv.nvfp4_kv_fp8_dequantize(caches[i], s_cal, outs[i]))(nxt()), 3 * n)
+    rate("kv_fp8_calibrate", lambda: (lambda i: nv.nvfp4_kv_fp8_calibrate(xs[i], s_cal, ws))(nxt()), 2 * n)
+    for k, v in res.items():
+        log(f"{k}: {v['us']} us = {v['GBps']} GB/s")
+    return {"kv_fp8_cache": {"workload": wl.name, "algorithmic_bytes_per_element": "write 3, read 3, calibrate 2",
+                             **res}}
 
 
 def secondary(nv, W, torch, np, dev, stream, log):

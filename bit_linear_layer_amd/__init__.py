@@ -76,6 +76,12 @@ def load() -> ctypes.CDLL:
         lib.nvfp4_gemm_swiglu.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), _P, _P, _I64,
                                           _P, ctypes.c_size_t, ctypes.POINTER(_Tensor), _P]
         lib.nvfp4_gemm_swiglu.restype = ctypes.c_int
+        lib.nvfp4_kv_fp8_calibrate.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P]
+        lib.nvfp4_kv_fp8_calibrate.restype = ctypes.c_int
+        lib.nvfp4_kv_fp8_quantize.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _P]
+        lib.nvfp4_kv_fp8_quantize.restype = ctypes.c_int
+        lib.nvfp4_kv_fp8_dequantize.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_int, _I64, _P]
+        lib.nvfp4_kv_fp8_dequantize.restype = ctypes.c_int
         lib.nvfp4_status_string.argtypes = [ctypes.c_int]
         lib.nvfp4_status_string.restype = ctypes.c_char_p
         lib.nvfp4_version.argtypes = []
@@ -222,6 +228,40 @@ def nvfp4_gemm_swiglu(a: NVFP4Tensor, w_gate_up: NVFP4Tensor, seg_global_scales:
     _check(st, "nvfp4_gemm_swiglu")
 
 
+def nvfp4_kv_fp8_calibrate(x: torch.Tensor, scale: torch.Tensor, workspace: torch.Tensor | None = None,
+                           stream=None) -> None:
+    """C ``nvfp4_kv_fp8_calibrate``: scale[0] = fl32(max|x| / 448)."""
+    ws = workspace if workspace is not None else workspace_for(x.shape[0], x.shape[1], x.device)
+    st = load().nvfp4_kv_fp8_calibrate(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
+                                       scale.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                       _stream(x.device, stream))
+    _check(st, "nvfp4_kv_fp8_calibrate")
+
+
+def nvfp4_kv_fp8_quantize(x: torch.Tensor, cache: torch.Tensor, scale: torch.Tensor,
+                          slots: torch.Tensor | None = None, stream=None) -> None:
+    """C ``nvfp4_kv_fp8_quantize``: E4M3 bytes of x / scale into cache rows
+    ``slots`` (int64 device tensor) or rows 0..len(x)-1."""
+    if x.dim() != 2 or x.stride(1) != 1 or cache.dim() != 2 or cache.stride(1) != 1:
+        raise NVFP4Error("x and cache must be 2-D with contiguous rows")
+    if slots is not None and (slots.dtype != torch.int64 or slots.numel() != x.shape[0]):
+        raise NVFP4Error("slots must be int64 with one entry per row of x")
+    st = load().nvfp4_kv_fp8_quantize(x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
+                                      _ptr(slots), cache.shape[0], cache.data_ptr(), cache.stride(0),
+                                      scale.data_ptr(), _stream(x.device, stream))
+    _check(st, "nvfp4_kv_fp8_quantize")
+
+
+def nvfp4_kv_fp8_dequantize(cache: torch.Tensor, scale: torch.Tensor, out: torch.Tensor, cols: int | None = None,
+                            stream=None) -> None:
+    """C ``nvfp4_kv_fp8_dequantize``: out = fl32(e4m3(cache) * scale) (bf16 out rounds that)."""
+    cols = out.shape[1] if cols is None else cols
+    st = load().nvfp4_kv_fp8_dequantize(cache.data_ptr(), out.shape[0], cols, cache.stride(0), scale.data_ptr(),
+                                        out.data_ptr(), _dtype_code(out), out.stride(0),
+                                        _stream(out.device, stream))
+    _check(st, "nvfp4_kv_fp8_dequantize")
+
+
 # ----------------------------------------------------------- conveniences
 
 def quantize(x: torch.Tensor, static_scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -276,3 +316,25 @@ def gemm_swiglu_quantized(a: NVFP4Tensor, w_gate_up: NVFP4Tensor, seg_global_sca
     q.global_scale.copy_(static_scale)
     nvfp4_gemm_swiglu(a, w_gate_up, seg_global_scales, h_q=q)
     return q
+
+
+def kv_fp8_quantize(x: torch.Tensor, scale: torch.Tensor, cache: torch.Tensor | None = None,
+                    slots: torch.Tensor | None = None) -> torch.Tensor:
+    """FP8 E4M3 bytes of x with the per-tensor decode scale ``scale``."""
+    c = cache if cache is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    nvfp4_kv_fp8_quantize(x, c, scale, slots)
+    return c
+
+
+def kv_fp8_dequantize(cache: torch.Tensor, scale: torch.Tensor, out_dtype=torch.bfloat16,
+                      cols: int | None = None) -> torch.Tensor:
+    cols = cache.shape[1] if cols is None else cols
+    out = torch.empty((cache.shape[0], cols), dtype=out_dtype, device=cache.device)
+    nvfp4_kv_fp8_dequantize(cache, scale, out, cols)
+    return out
+
+
+def kv_fp8_calibrate(x: torch.Tensor) -> torch.Tensor:
+    s = torch.empty(1, dtype=torch.float32, device=x.device)
+    nvfp4_kv_fp8_calibrate(x, s)
+    return s

@@ -227,6 +227,55 @@ int nvfp4_silu_mul(const void* gu, int64_t rows, int64_t inter, int64_t ld_gu, v
                                     (float*)amax_workspace, np, (hipStream_t)stream));
 }
 
+int nvfp4_kv_fp8_calibrate(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           float* scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (x == nullptr || scale == nullptr || workspace == nullptr) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows >= kIndexLimit || cols >= kIndexLimit) return NVFP4_ERR_RANGE;
+  const int esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (ld_x < cols || (ld_x * esz) % 16 != 0) return NVFP4_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(scale, 4) || !aligned(workspace, 4)) return NVFP4_ERR_ALIGN;
+  const int np = partial_count(rows, cols, 16);
+  if (workspace_bytes < sizeof(float) * (size_t)np) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int st = hip_status(launch_amax(x, x_dtype, rows, cols, ld_x, (float*)workspace, np, s));
+  if (st != NVFP4_OK) return st;
+  return hip_status(launch_kv_scale((const float*)workspace, np, scale, s));
+}
+
+int nvfp4_kv_fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                          const int64_t* slots, int64_t cache_rows, uint8_t* cache, int64_t ld_cache,
+                          const float* scale, void* stream) {
+  if (x == nullptr || cache == nullptr || scale == nullptr) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || cache_rows <= 0) return NVFP4_ERR_SHAPE;
+  if (rows >= kIndexLimit || cols >= kIndexLimit || cache_rows >= kIndexLimit) return NVFP4_ERR_RANGE;
+  if (slots == nullptr && cache_rows < rows) return NVFP4_ERR_SHAPE;
+  const int esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (ld_x < cols || (ld_x * esz) % 16 != 0) return NVFP4_ERR_STRIDE;
+  if (ld_cache < cols || ld_cache % 8 != 0) return NVFP4_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(cache, 8) || !aligned(scale, 4) || !aligned(slots, 8))
+    return NVFP4_ERR_ALIGN;
+  return hip_status(launch_kv_quantize(x, x_dtype, rows, cols, ld_x, slots, cache_rows, cache, ld_cache,
+                                       scale, (hipStream_t)stream));
+}
+
+int nvfp4_kv_fp8_dequantize(const uint8_t* cache, int64_t rows, int64_t cols, int64_t ld_cache,
+                            const float* scale, void* out, int out_dtype, int64_t ld_out,
+                            void* stream) {
+  if (cache == nullptr || scale == nullptr || out == nullptr) return NVFP4_ERR_NULL;
+  if (out_dtype != NVFP4_DTYPE_BF16 && out_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows >= kIndexLimit || cols >= kIndexLimit) return NVFP4_ERR_RANGE;
+  const int esz = out_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (ld_cache < cols || ld_cache % 8 != 0) return NVFP4_ERR_STRIDE;
+  if (ld_out < cols || (ld_out * esz) % 16 != 0) return NVFP4_ERR_STRIDE;
+  if (!aligned(cache, 8) || !aligned(scale, 4) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  return hip_status(launch_kv_dequantize(cache, rows, cols, ld_cache, scale, out, out_dtype, ld_out,
+                                         (hipStream_t)stream));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

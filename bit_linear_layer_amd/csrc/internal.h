@@ -72,6 +72,15 @@ hipError_t launch_gemm_swiglu(const GemmArgs& args, hipStream_t s);
 
 hipError_t launch_zero(float* p, int n, hipStream_t s);
 
+// FP8 (E4M3) KV cache with a per-tensor scale (kv_fp8.hip).
+hipError_t launch_kv_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              const int64_t* slots, int64_t cache_rows, uint8_t* cache,
+                              int64_t ld_cache, const float* scale, hipStream_t s);
+hipError_t launch_kv_dequantize(const uint8_t* cache, int64_t rows, int64_t cols, int64_t ld_cache,
+                                const float* scale, void* out, int out_dtype, int64_t ld_out,
+                                hipStream_t s);
+hipError_t launch_kv_scale(const float* partials, int n, float* scale, hipStream_t s);
+
 // Small-M (decode) path over the columns [n_lo, n_hi) when skinny_eligible().
 bool skinny_eligible(const GemmArgs& p);
 hipError_t launch_gemm_skinny(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s);

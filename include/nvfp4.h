@@ -213,6 +213,44 @@ int nvfp4_gemm_swiglu(const nvfp4_tensor* a, const nvfp4_tensor* w_gate_up,
                       void* amax_workspace, size_t workspace_bytes, const nvfp4_tensor* h_q,
                       void* stream);
 
+/*
+ * FP8 (E4M3) KV cache with a calibrated per-tensor scale (evolve.pub review,
+ * "Key claims under review", fifth claim: calibrated per-tensor FP8 KV-cache
+ * scales; chatpaper.ai English abstract).  The scale s (DEVICE float32 [1])
+ * is a decode multiplier: a cached byte q stands for e4m3(q) * s.  s = 1 is
+ * the uncalibrated cache; calibrated and uncalibrated caches run the same
+ * kernels.  Rows are cols elements, cols % 16 == 0.  Codes 0x7F/0xFF (NaN)
+ * never come out of the write and are outside the contract of the read.
+ *
+ * nvfp4_kv_fp8_calibrate -- *scale = fl32(max|x| / 448) over x [rows, cols]
+ *   (bf16 or float32, ld_x elements, rows 16-byte aligned).  workspace:
+ *   nvfp4_quantize_workspace_bytes(rows, cols) bytes of device memory.
+ */
+int nvfp4_kv_fp8_calibrate(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           float* scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_kv_fp8_quantize -- write x [rows, cols] (bf16 or float32) into the
+ * cache: cache[slot(i), j] = E4M3 byte nearest to the exact real x[i, j] / s,
+ * ties to even code, |x / s| beyond 448 saturating to +-448, sign bit = IEEE
+ * sign of x.  slot(i) = slots[i] (DEVICE int64 [rows]) or i when slots is
+ * NULL; rows whose slot lies outside [0, cache_rows) are not written.
+ * cache: DEVICE uint8 [cache_rows, ld_cache], ld_cache % 8 == 0, 8-byte
+ * aligned; x rows 16-byte aligned.
+ */
+int nvfp4_kv_fp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                          const int64_t* slots, int64_t cache_rows, uint8_t* cache, int64_t ld_cache,
+                          const float* scale, void* stream);
+
+/*
+ * nvfp4_kv_fp8_dequantize -- out[i, j] = fl32(e4m3(cache[i, j]) * s) (one
+ * rounding of the exact product), stored as float32 or rounded to bf16
+ * (nearest even).  out: DEVICE [rows, ld_out] elements, rows 16-byte aligned.
+ */
+int nvfp4_kv_fp8_dequantize(const uint8_t* cache, int64_t rows, int64_t cols, int64_t ld_cache,
+                            const float* scale, void* out, int out_dtype, int64_t ld_out,
+                            void* stream);
+
 /* Human-readable text of a status (and of the last HIP error, for NVFP4_ERR_HIP). */
 const char* nvfp4_status_string(int status);
 

@@ -133,3 +133,28 @@ def swiglu(a=None, w=None, sg=FAKE, h=FAKE, ldh=16, ws=None, wsb=0, hq=None):
 ])
 def test_swiglu_rejects_bad_arguments(kw, status):
     assert swiglu(**kw) == status
+
+
+def test_kv_fp8_entry_points_reject_bad_arguments():
+    lib = nv.load()
+    cal = lib.nvfp4_kv_fp8_calibrate
+    assert cal(None, 0, 4, 32, 32, FAKE, FAKE, 4096, None) == -1
+    assert cal(FAKE, 0, 4, 32, 32, FAKE, None, 4096, None) == -1
+    assert cal(FAKE, 3, 4, 32, 32, FAKE, FAKE, 4096, None) == -3
+    assert cal(FAKE, 0, 4, 24, 24, FAKE, FAKE, 4096, None) == -2
+    assert cal(FAKE, 0, 4, 32, 36, FAKE, FAKE, 4096, None) == -4
+    assert cal(FAKE, 0, 4, 32, 32, FAKE, FAKE, 0, None) == -8
+    qz = lib.nvfp4_kv_fp8_quantize
+    assert qz(FAKE, 0, 4, 32, 32, None, 4, None, 32, FAKE, None) == -1
+    assert qz(FAKE, 0, 4, 32, 32, None, 3, FAKE, 32, FAKE, None) == -2  # too few cache rows without slots
+    assert qz(FAKE, 0, 4, 32, 32, None, 4, FAKE, 36, FAKE, None) == -4
+    assert qz(FAKE, 0, 4, 32, 32, None, 4, FAKE, 16, FAKE, None) == -4
+    assert qz(FAKE, 0, 4, 32, 32, FAKE + 4, 4, FAKE, 32, FAKE, None) == -5
+    assert qz(FAKE + 8, 0, 4, 32, 32, None, 4, FAKE, 32, FAKE, None) == -5
+    assert qz(FAKE, 0, 4, 32, 32, None, 1 << 31, FAKE, 32, FAKE, None) == -11
+    dq = lib.nvfp4_kv_fp8_dequantize
+    assert dq(FAKE, 4, 32, 32, None, FAKE, 0, 32, None) == -1
+    assert dq(FAKE, 4, 32, 32, FAKE, FAKE, 2, 32, None) == -3
+    assert dq(FAKE, 4, 40, 40, FAKE, FAKE, 0, 40, None) == -2
+    assert dq(FAKE, 4, 32, 32, FAKE, FAKE, 1, 34, None) == -4
+    assert dq(FAKE, 4, 32, 32, FAKE, FAKE + 8, 0, 32, None) == -5

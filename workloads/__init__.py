@@ -141,6 +141,15 @@ def decode(seed: int = 0, m: int = 8, k: int = 5120, inter: int = 17408) -> Work
     return Workload(f"decode_m{m}_n{2 * inter}_k{k}", to_bf16(x), [("gate", w_gate), ("up", w_up)])
 
 
+def kv_cache(seed: int = 0, tokens: int = 32768, heads: int = 8, head_dim: int = 128) -> Workload:
+    """One layer's K tensor for the FP8 KV cache: [tokens, heads*head_dim]
+    bf16, N(0,1) with 8 channels x10 (keys carry outlier channels).  The
+    pages give no KV dimensions; 32K tokens is their long-context length."""
+    rng = np.random.default_rng(seed)
+    x = outlier_activations(rng, tokens, heads * head_dim, heavy=False, n_outlier=8, factor=10.0)
+    return Workload(f"kv_cache_t{tokens}_h{heads}_d{head_dim}", to_bf16(x), [])
+
+
 def random_bf16(seed: int, rows: int, cols: int, scale: float = 1.0) -> torch.Tensor:
     rng = np.random.default_rng(seed)
     return to_bf16(rng.standard_normal(size=(rows, cols)) * scale)
