@@ -387,3 +387,45 @@ def kv_fp8_dequantize(q, s, out_dtype: str = "f32") -> np.ndarray:
     if out_dtype == "bf16":
         return round_bf16(prod.astype(np.float64))
     raise ValueError(out_dtype)
+
+
+# ---------------------------------------------------------------------------
+# Checkpoint-side scale harmonization of fused modules
+# ---------------------------------------------------------------------------
+# Sources: evolve.pub review, "Key claims under review", fourth claim (per-
+# module NVFP4 calibration served by fused GEMMs corrupts the GDN gates; a
+# checkpoint-side scale harmonization repairs it); chatpaper.ai English
+# abstract (the global-scale mismatch of fused modules).  Readings (the pages
+# give no procedure): the modules fused into one GEMM share the common global
+# scale G = max_s g_s (the scale their concatenation would get, since fl32
+# rounding is monotone in amax); every block scale of segment s is rewritten
+# to the E4M3 value nearest to the exact real e4m3(b) * g_s / G (ties to the
+# even code; the ratio is <= 1, so nothing saturates); E2M1 codes are kept.
+# A kernel that applies one global scale per weight then serves the group up
+# to that scale rounding; serving the per-module checkpoint with one module's
+# scale is the mismatch.
+#
+# Exactness: e4m3(b) * g_s has <= 28 significant bits (exact in float64) and
+# G has 24; a non-tie quotient lies >= ~2^-30 (relative) from every E4M3
+# midpoint, and a tie divides exactly, so rounding the float64 quotient takes
+# the exact-real decision.
+
+def harmonized_global_scale(seg_g) -> np.float32:
+    """Common global scale of a fused group: the largest module scale."""
+    return np.float32(max(float(np.float32(g)) for g in seg_g))
+
+
+def harmonize_scales(w_scales, seg_offsets, seg_g):
+    """Block scales of a segmented NVFP4 weight rewritten for the common
+    global scale G.  Returns (scales uint8 [N, K/16], G float32)."""
+    w_scales = np.asarray(w_scales, dtype=np.uint8)
+    if np.any(w_scales > 0x7E):
+        raise ValueError("scale bytes must be non-negative finite E4M3 (0x00..0x7E)")
+    G = harmonized_global_scale(seg_g)
+    seg_offsets = [int(o) for o in seg_offsets]
+    out = np.empty_like(w_scales)
+    for s in range(len(seg_offsets) - 1):
+        r0, r1 = seg_offsets[s], seg_offsets[s + 1]
+        ratio_num = E4M3_VALUES[w_scales[r0:r1]] * float(np.float32(seg_g[s]))  # exact
+        out[r0:r1] = round_e4m3(ratio_num / float(G))
+    return out, G

@@ -105,3 +105,21 @@ def bf16_nearest(v: Fraction) -> float:
             cands.append((abs(Fraction(float(val)) - v), (b >> 16) & 1, float(val)))
     cands.sort()
     return cands[0][2]
+
+
+def nearest_e4m3_byte(r) -> int:
+    """E4M3 byte (0x00..0x7E) nearest to the exact rational r >= 0 by
+    exhaustive search over all finite values built from the bit definition;
+    ties to the even code; r beyond 448 saturates."""
+    from fractions import Fraction
+    vals = [Fraction(m, 2 ** 9) for m in range(8)] + [
+        Fraction(8 + (b & 7), 8) * Fraction(2) ** ((b >> 3) - 7) for b in range(8, 0x7F)]
+    r = Fraction(r)
+    if r > vals[-1]:
+        return 0x7E
+    best = None
+    for b, v in enumerate(vals):
+        d = abs(r - v)
+        if best is None or d < best[0] or (d == best[0] and b % 2 == 0):
+            best = (d, b)
+    return best[1]
