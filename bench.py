@@ -366,7 +366,36 @@ def secondary(nv, W, torch, np, dev, stream, log):
                                  "TFLOPs_incl_act_quant": round(fl / t / 1e12, 1),
                                  "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
     log(f"gdn in-proj: {t * 1e3:.3f} ms = {fl / t / 1e12:.0f} TFLOP/s")
+    res["scale_harmonization_gdn_in_proj"] = harmonization_study(nv, torch, stream, log, gw, ag, wq, offs, sg, gate)
     return res
+
+
+def harmonization_study(nv, torch, stream, log, gw, ag, wq, offs, sg, gate):
+    """The global-scale mismatch and its checkpoint-side repair on the 32K
+    GDN in-projection with gates: per module, the relative error against the
+    per-module-scale result (this library's fused epilogue) of (a) serving
+    module q's scale for every column and (b) the harmonized weight served
+    with one global scale; plus the harmonization kernel's time."""
+    n = len(offs) - 1
+    hw = nv.harmonize_scales(wq, offs, sg)
+    hs_buf, g_buf = torch.empty_like(wq.scales), torch.empty(1, dtype=torch.float32, device=wq.codes.device)
+    t_h = time_steps(torch, stream, lambda: nv.nvfp4_harmonize_scales(wq, offs, sg, hs_buf, g_buf), steps=20)
+    ref = nv.gemm_fused_segments(ag, wq, offs, sg, gate, out_dtype=torch.float32)
+    fixed = nv.gemm_fused_segments(ag, hw, offs, hw.global_scale.repeat(n), gate, out_dtype=torch.float32)
+    bad = nv.gemm_fused_segments(ag, wq, offs, sg[:1].repeat(n), gate, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    names = [nm for nm, _ in gw.weights]
+    per = {}
+    for i, nm in enumerate(names):
+        c = slice(offs[i], offs[i + 1])
+        den = torch.linalg.vector_norm(ref[:, c].double()).item()
+        per[nm] = {"harmonized": round(torch.linalg.vector_norm((fixed[:, c] - ref[:, c]).double()).item() / den, 6),
+                   "mismatch": round(torch.linalg.vector_norm((bad[:, c] - ref[:, c]).double()).item() / den, 6)}
+    del ref, fixed, bad
+    log("harmonization: " + ", ".join(f"{k} {v['harmonized']:.4f}/{v['mismatch']:.4f}" for k, v in per.items()))
+    return {"relative_error_vs_per_module_scales": per,
+            "outputs": "b and a columns are the gate outputs (sigmoid, decay) of each variant",
+            "harmonize_kernel_us": round(t_h * 1e3, 2)}
 
 
 def cpu_baseline(nv, W, torch, np, wl, a, w_gu, gu_offs, gu_g, w_d, d_offs, d_g, rows, log):

@@ -82,6 +82,9 @@ def load() -> ctypes.CDLL:
         lib.nvfp4_kv_fp8_quantize.restype = ctypes.c_int
         lib.nvfp4_kv_fp8_dequantize.argtypes = [_P, _I64, _I64, _I64, _P, _P, ctypes.c_int, _I64, _P]
         lib.nvfp4_kv_fp8_dequantize.restype = ctypes.c_int
+        lib.nvfp4_harmonize_scales.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                               _P, _P, _I64, _P, _P]
+        lib.nvfp4_harmonize_scales.restype = ctypes.c_int
         lib.nvfp4_status_string.argtypes = [ctypes.c_int]
         lib.nvfp4_status_string.restype = ctypes.c_char_p
         lib.nvfp4_version.argtypes = []
@@ -262,6 +265,19 @@ def nvfp4_kv_fp8_dequantize(cache: torch.Tensor, scale: torch.Tensor, out: torch
     _check(st, "nvfp4_kv_fp8_dequantize")
 
 
+def nvfp4_harmonize_scales(w: NVFP4Tensor, seg_offsets, seg_global_scales: torch.Tensor,
+                           out_scales: torch.Tensor, out_global_scale: torch.Tensor, stream=None) -> None:
+    """C ``nvfp4_harmonize_scales``: block scales of every segment rewritten
+    for the common global scale max(seg_global_scales) (written to
+    out_global_scale); E2M1 codes unchanged."""
+    offs = (ctypes.c_int64 * len(seg_offsets))(*[int(o) for o in seg_offsets])
+    dw = w.descriptor()
+    st = load().nvfp4_harmonize_scales(ctypes.byref(dw), len(seg_offsets) - 1, offs, seg_global_scales.data_ptr(),
+                                       out_scales.data_ptr(), out_scales.stride(0), out_global_scale.data_ptr(),
+                                       _stream(w.codes.device, stream))
+    _check(st, "nvfp4_harmonize_scales")
+
+
 # ----------------------------------------------------------- conveniences
 
 def quantize(x: torch.Tensor, static_scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -338,3 +354,11 @@ def kv_fp8_calibrate(x: torch.Tensor) -> torch.Tensor:
     s = torch.empty(1, dtype=torch.float32, device=x.device)
     nvfp4_kv_fp8_calibrate(x, s)
     return s
+
+
+def harmonize_scales(w: NVFP4Tensor, seg_offsets, seg_global_scales: torch.Tensor) -> NVFP4Tensor:
+    """The harmonized weight: w's codes, new block scales, one global scale."""
+    scales = torch.empty_like(w.scales)
+    g = torch.empty(1, dtype=torch.float32, device=w.codes.device)
+    nvfp4_harmonize_scales(w, seg_offsets, seg_global_scales, scales, g)
+    return NVFP4Tensor(w.codes, scales, g, w.rows, w.cols)

@@ -276,6 +276,30 @@ int nvfp4_kv_fp8_dequantize(const uint8_t* cache, int64_t rows, int64_t cols, in
                                          (hipStream_t)stream));
 }
 
+int nvfp4_harmonize_scales(const nvfp4_tensor* w, int n_segments, const int64_t* seg_offsets,
+                           const float* seg_global_scales, uint8_t* out_scales,
+                           int64_t ld_out_scales, float* out_global_scale, void* stream) {
+  if (w == nullptr || w->scales == nullptr) return NVFP4_ERR_NULL;
+  if (seg_offsets == nullptr || seg_global_scales == nullptr || out_scales == nullptr ||
+      out_global_scale == nullptr)
+    return NVFP4_ERR_NULL;
+  if (w->rows <= 0 || w->cols <= 0 || w->cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (w->rows >= kIndexLimit || w->cols >= kIndexLimit) return NVFP4_ERR_RANGE;
+  if (w->ld_scales < w->cols / 16 || ld_out_scales < w->cols / 16) return NVFP4_ERR_STRIDE;
+  if (!aligned(out_global_scale, 4)) return NVFP4_ERR_ALIGN;
+  if (n_segments < 1 || n_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_SEGMENTS;
+  if (seg_offsets[0] != 0 || seg_offsets[n_segments] != w->rows) return NVFP4_ERR_SEGMENTS;
+  SegmentTable seg{};
+  seg.n = n_segments;
+  for (int s = 0; s <= n_segments; ++s) {
+    if (s > 0 && seg_offsets[s] <= seg_offsets[s - 1]) return NVFP4_ERR_SEGMENTS;
+    seg.off[s] = seg_offsets[s];
+  }
+  return hip_status(launch_harmonize(w->scales, w->ld_scales, out_scales, ld_out_scales, w->rows,
+                                     w->cols / 16, seg, seg_global_scales, out_global_scale,
+                                     (hipStream_t)stream));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

@@ -81,6 +81,15 @@ hipError_t launch_kv_dequantize(const uint8_t* cache, int64_t rows, int64_t cols
                                 hipStream_t s);
 hipError_t launch_kv_scale(const float* partials, int n, float* scale, hipStream_t s);
 
+// Checkpoint-side scale harmonization (harmonize.hip).
+struct SegmentTable {
+  int n;
+  int64_t off[NVFP4_MAX_SEGMENTS + 1];
+};
+hipError_t launch_harmonize(const uint8_t* in, int64_t ld_in, uint8_t* out, int64_t ld_out,
+                            int64_t rows, int64_t bpr, const SegmentTable& seg, const float* seg_g,
+                            float* g_out, hipStream_t s);
+
 // Small-M (decode) path over the columns [n_lo, n_hi) when skinny_eligible().
 bool skinny_eligible(const GemmArgs& p);
 hipError_t launch_gemm_skinny(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s);

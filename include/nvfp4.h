@@ -251,6 +251,29 @@ int nvfp4_kv_fp8_dequantize(const uint8_t* cache, int64_t rows, int64_t cols, in
                             const float* scale, void* out, int out_dtype, int64_t ld_out,
                             void* stream);
 
+/*
+ * nvfp4_harmonize_scales -- checkpoint-side repair of the global-scale
+ * mismatch (evolve.pub review, "Key claims under review", fourth claim;
+ * chatpaper.ai English abstract): per-module calibrated segments of a fused
+ * weight are rewritten to share one global scale, so that a GEMM applying a
+ * single global scale serves them.  G = max_s seg_global_scales[s]; every
+ * block scale byte b of segment s becomes the E4M3 byte nearest to the exact
+ * real e4m3(b) * g_s / G, ties to the even code.  E2M1 codes are unchanged:
+ * the harmonized weight is {w->codes, out_scales, out_global_scale}.
+ *
+ *   w                  the segmented weight; only its scales are read
+ *                      (w->global_scale is not used and may be NULL).
+ *   seg_offsets        HOST int64 [n_segments + 1], as for
+ *                      nvfp4_gemm_fused_segments; seg_global_scales DEVICE
+ *                      float32 [n_segments], positive.
+ *   out_scales         DEVICE uint8 [w->rows, ld_out_scales], ld_out_scales
+ *                      >= w->cols / 16; may be w->scales (in place).
+ *   out_global_scale   DEVICE float32 [1], receives G.
+ */
+int nvfp4_harmonize_scales(const nvfp4_tensor* w, int n_segments, const int64_t* seg_offsets,
+                           const float* seg_global_scales, uint8_t* out_scales,
+                           int64_t ld_out_scales, float* out_global_scale, void* stream);
+
 /* Human-readable text of a status (and of the last HIP error, for NVFP4_ERR_HIP). */
 const char* nvfp4_status_string(int status);
 

@@ -158,3 +158,18 @@ def test_kv_fp8_entry_points_reject_bad_arguments():
     assert dq(FAKE, 4, 40, 40, FAKE, FAKE, 0, 40, None) == -2
     assert dq(FAKE, 4, 32, 32, FAKE, FAKE, 1, 34, None) == -4
     assert dq(FAKE, 4, 32, 32, FAKE, FAKE + 8, 0, 32, None) == -5
+
+
+def test_harmonize_rejects_bad_arguments():
+    f = nv.load().nvfp4_harmonize_scales
+
+    def call(w=None, n=2, offs=(0, 4, 8), sg=FAKE, out=FAKE, ld=8, g=FAKE):
+        w = w or tensor(rows=8)
+        arr = (ctypes.c_int64 * len(offs))(*offs)
+        return f(ctypes.byref(w), n, arr, sg, out, ld, g, None)
+    assert call(sg=None) == -1 and call(out=None) == -1 and call(g=None) == -1
+    assert call(w=tensor(rows=8, scales=0)) == -1
+    assert call(w=tensor(rows=8, cols=24)) == -2
+    assert call(ld=1) == -4
+    assert call(g=FAKE + 2) == -5
+    assert call(n=0, offs=(0,)) == -6 and call(offs=(0, 4, 7)) == -6 and call(offs=(0, 9, 8)) == -6
