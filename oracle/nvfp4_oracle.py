@@ -429,3 +429,63 @@ def harmonize_scales(w_scales, seg_offsets, seg_g):
         ratio_num = E4M3_VALUES[w_scales[r0:r1]] * float(np.float32(seg_g[s]))  # exact
         out[r0:r1] = round_e4m3(ratio_num / float(G))
     return out, G
+
+
+# ---------------------------------------------------------------------------
+# Gated delta-rule recurrence (the GDN state update consuming beta and g)
+# ---------------------------------------------------------------------------
+# Sources: chatpaper.ai English abstract, mechanism (iii) (the delta-rule
+# recurrence holds injected noise at a plateau and forgets a state impulse
+# because each write overwrites the state along the current key direction)
+# and mechanism (ii) (write strength through a sigmoid, decay through a
+# log-space softplus/exponential); evolve.pub review, "Key claims under
+# review", third claim and "Strengths" (relS plateau, impulse erasure).  The
+# pages name Gated DeltaNet but do not write its update; this is the
+# published gated delta rule, per value head h with state S in R^{dv x dk}:
+#
+#     S_t = exp(g_t) * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+#     o_t = S_t q_t
+#
+# beta_t = sigmoid(b-gate), g_t = -exp(A_log) * softplus(a-gate + dt_bias)
+# (the gate epilogue's outputs, a log-space decay <= 0).  Readings: q and k
+# heads are shared by groups of value heads (value head h reads q/k head
+# h // (Hv / Hk)); with normalize=True q and k are L2-normalized over the
+# head dimension first and q is scaled by dk^-1/2 (the short convolution
+# that precedes them in a GDN layer is outside this path).
+
+def l2_normalize(x) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, 1e-30)
+
+
+def gdn_recurrence(q, k, v, beta, g, s0=None, normalize: bool = True):
+    """Sequential gated delta rule in float64.
+
+    q, k: [T, Hk, dk]; v: [T, Hv, dv]; beta, g: [T, Hv]; s0: [Hv, dv, dk] or
+    None (zeros).  Returns (o [T, Hv, dv], s_final [Hv, dv, dk])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    T, hk, dk = k.shape
+    hv, dv = v.shape[1], v.shape[2]
+    if hv % hk != 0:
+        raise ValueError("value heads must be a multiple of key heads")
+    if normalize:
+        q = l2_normalize(q) / math.sqrt(dk)
+        k = l2_normalize(k)
+    rep = hv // hk
+    qh = np.repeat(q, rep, axis=1)  # [T, Hv, dk]
+    kh = np.repeat(k, rep, axis=1)
+    s = np.zeros((hv, dv, dk)) if s0 is None else np.array(s0, dtype=np.float64)
+    o = np.empty((T, hv, dv))
+    for t in range(T):
+        kt, qt = kh[t], qh[t]                      # [Hv, dk]
+        a = np.exp(g[t])[:, None, None]            # decay factor
+        b = beta[t][:, None]                       # [Hv, 1]
+        sk = np.einsum("hij,hj->hi", s, kt)        # S_{t-1} k_t
+        s = a * s - (a[:, :, 0] * b * sk)[:, :, None] * kt[:, None, :] + (b * v[t])[:, :, None] * kt[:, None, :]
+        o[t] = np.einsum("hij,hj->hi", s, qt)
+    return o, s
