@@ -367,7 +367,110 @@ def secondary(nv, W, torch, np, dev, stream, log):
                                  "frac_of_mfma_peak": round(fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
     log(f"gdn in-proj: {t * 1e3:.3f} ms = {fl / t / 1e12:.0f} TFLOP/s")
     res["scale_harmonization_gdn_in_proj"] = harmonization_study(nv, torch, stream, log, gw, ag, wq, offs, sg, gate)
+    del outg
+    res["gdn_recurrence"] = gdn_study(nv, W, torch, stream, log, dev)
     return res
+
+
+def gdn_study(nv, W, torch, stream, log, dev):
+    """The gated delta-rule recurrence of one synthetic GDN layer (32K tokens,
+    48 value heads, 16 key heads, 128 wide; gate projections scaled to the
+    pages' decay horizons): its time, and the pages' two recurrence
+    measurements -- relS, the relative state error of
+    the NVFP4-quantized layer against an unquantized (bf16 weights and
+    activations, float32 products) in-projection, along the sequence; and the
+    erasure of a state impulse (10 % of |S|) injected at token 8192, in steps
+    until it falls below 1/e and 10 %, beside each head's pure-decay horizon
+    1 / mean(-g)."""
+    gw = W.gdn_layer()
+    xg = gw.x.to(dev)
+    T = xg.shape[0]
+    segs = [t.to(dev) for _, t in gw.weights]
+    wq = nv.empty_nvfp4(sum(t.shape[0] for t in segs), xg.shape[1], dev)
+    sg = torch.empty(len(segs), dtype=torch.float32, device=dev)
+    offs = [0]
+    wsq = nv.workspace_for(max(t.shape[0] for t in segs), xg.shape[1], dev)
+    for i, t in enumerate(segs):
+        part = wq.row_slice(offs[-1], offs[-1] + t.shape[0])
+        nv.nvfp4_quantize(t, nv.NVFP4Tensor(part.codes, part.scales, sg[i:i + 1], part.rows, part.cols),
+                          nv.SCALE_DYNAMIC, wsq)
+        offs.append(offs[-1] + t.shape[0])
+    gate = dict(b_segment=4, a_segment=5, A_log=gw.extra["A_log"].to(dev), dt_bias=gw.extra["dt_bias"].to(dev))
+    ag = nv.quantize(xg)
+    hk, hv = (offs[1] - offs[0]) // 128, (offs[3] - offs[2]) // 128
+    outq = nv.gemm_fused_segments(ag, wq, offs, sg, gate, out_dtype=torch.float32)
+    cols = lambda o, s: o[:, offs[s]:offs[s + 1]]
+    ws = torch.empty(nv.nvfp4_gdn_workspace_bytes(T, hv) // 4, dtype=torch.float32, device=dev)
+    o = torch.empty((T, hv * 128), dtype=torch.float32, device=dev)
+    run = lambda src: nv.nvfp4_gdn_recurrence(cols(src, 0), cols(src, 1), cols(src, 2), cols(src, 4), cols(src, 5),
+                                              o, hk, hv, ws)
+    ms = time_steps(torch, stream, lambda: run(outq), steps=3, warmup=1)
+    flops = 8.0 * 128 * 128 * T * hv  # S k, two rank-1 updates, S q per token and head
+    log(f"gdn recurrence {T} tokens x {hv} heads: {ms:.2f} ms = {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s (fp32)")
+
+    # unquantized reference in-projection with the same gate formulas
+    w = torch.cat(segs).float()
+    del segs
+    ref = xg.float() @ w.t()
+    del w
+    b0, a0 = offs[4], offs[5]
+    a_log, dt_bias = gate["A_log"].float(), gate["dt_bias"].float()
+    ref[:, b0:offs[5]] = torch.sigmoid(ref[:, b0:offs[5]])
+    ref[:, a0:offs[6]] = -torch.exp(a_log) * torch.nn.functional.softplus(ref[:, a0:offs[6]] + dt_bias)
+
+    def states(src, bounds, s_init=None, t_begin=0):
+        """States after each prefix end in `bounds`, carrying the state across calls."""
+        out, s = [], s_init
+        t_prev = t_begin
+        for t_end in bounds:
+            sl = slice(t_prev, t_end)
+            wsl = torch.empty(nv.nvfp4_gdn_workspace_bytes(t_end - t_prev, hv) // 4, dtype=torch.float32, device=dev)
+            osl = torch.empty((t_end - t_prev, hv * 128), dtype=torch.float32, device=dev)
+            s_new = torch.empty((hv, 128, 128), dtype=torch.float32, device=dev)
+            nv.nvfp4_gdn_recurrence(cols(src, 0)[sl], cols(src, 1)[sl], cols(src, 2)[sl], cols(src, 4)[sl],
+                                    cols(src, 5)[sl], osl, hk, hv, wsl, s0=s, s_final=s_new)
+            out.append(s_new)
+            s, t_prev = s_new, t_end
+        return out
+
+    marks = [256, 1024] + list(range(2048, T + 1, 2048))
+    sq_, sr_ = states(outq, marks), states(ref, marks)
+    rel = [((a - b).flatten(1).norm(dim=1) / b.flatten(1).norm(dim=1)) for a, b in zip(sq_, sr_)]
+    rels = {str(m): {"mean": round(r.mean().item(), 4), "min": round(r.min().item(), 4), "max": round(r.max().item(), 4)}
+            for m, r in zip(marks, rel)}
+    log("relS mean: " + ", ".join(f"{m}:{v['mean']:.3f}" for m, v in rels.items()))
+
+    # impulse erasure on the reference dynamics
+    t0 = 8192
+    s_t0 = states(ref, [t0])[0]
+    gen = torch.Generator(device=dev).manual_seed(0)
+    imp = torch.randn(s_t0.shape, device=dev, generator=gen)
+    imp *= (0.1 * s_t0.flatten(1).norm(dim=1) / imp.flatten(1).norm(dim=1))[:, None, None]
+    ends = list(range(t0 + 16, t0 + 1025, 16)) + list(range(t0 + 1152, min(T, t0 + 8192) + 1, 128))
+    base = states(ref, ends, s_init=s_t0, t_begin=t0)
+    pert = states(ref, ends, s_init=s_t0 + imp, t_begin=t0)
+    norm0 = imp.flatten(1).norm(dim=1)
+    ratio = torch.stack([(p_ - b_).flatten(1).norm(dim=1) / norm0 for p_, b_ in zip(pert, base)])  # [steps, hv]
+    steps = torch.tensor([e - t0 for e in ends], device=dev, dtype=torch.float32)
+
+    def first_below(th):
+        below = ratio < th
+        idx = torch.where(below.any(dim=0), below.float().argmax(dim=0), torch.full((hv,), len(ends) - 1, device=dev))
+        return steps[idx]
+    e1, e10 = first_below(float(torch.exp(torch.tensor(-1.0)))), first_below(0.1)
+    horizon = 1.0 / (-ref[:, a0:offs[6]].mean(dim=0))
+    imp_res = {"steps_to_1_over_e": {"median": e1.median().item(), "min": e1.min().item(), "max": e1.max().item()},
+               "steps_to_10pct": {"median": e10.median().item(), "min": e10.min().item(), "max": e10.max().item()},
+               "pure_decay_horizon_tokens": {"median": round(horizon.median().item(), 1),
+                                             "min": round(horizon.min().item(), 1),
+                                             "max": round(horizon.max().item(), 1)},
+               "resolution_tokens": "16 up to 1024 steps, then 128"}
+    log(f"impulse: 1/e after median {imp_res['steps_to_1_over_e']['median']:.0f} steps "
+        f"(pure-decay horizon median {imp_res['pure_decay_horizon_tokens']['median']:.0f} tokens)")
+    del ref, outq
+    return {"ms": round(ms, 3), "tflops_fp32": round(flops / (ms * 1e-3) / 1e12, 2),
+            "algorithmic_flops": flops, "relS_vs_unquantized": rels, "impulse_erasure": imp_res,
+            "note": "q and k L2-normalized straight from the in-projection (no short convolution)"}
 
 
 def harmonization_study(nv, torch, stream, log, gw, ag, wq, offs, sg, gate):

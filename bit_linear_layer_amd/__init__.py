@@ -46,6 +46,12 @@ class _Gate(ctypes.Structure):
                 ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
 
 
+class _GdnInputs(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("ld_q", ctypes.c_int64), ("k", ctypes.c_void_p), ("ld_k", ctypes.c_int64),
+                ("v", ctypes.c_void_p), ("ld_v", ctypes.c_int64), ("beta", ctypes.c_void_p),
+                ("ld_beta", ctypes.c_int64), ("g", ctypes.c_void_p), ("ld_g", ctypes.c_int64)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -85,6 +91,11 @@ def load() -> ctypes.CDLL:
         lib.nvfp4_harmonize_scales.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
                                                _P, _P, _I64, _P, _P]
         lib.nvfp4_harmonize_scales.restype = ctypes.c_int
+        lib.nvfp4_gdn_workspace_bytes.argtypes = [_I64, ctypes.c_int]
+        lib.nvfp4_gdn_workspace_bytes.restype = ctypes.c_size_t
+        lib.nvfp4_gdn_recurrence.argtypes = [ctypes.POINTER(_GdnInputs), ctypes.c_int, _I64, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, _P, _P, _P, ctypes.c_int, _I64, _P, ctypes.c_size_t, _P]
+        lib.nvfp4_gdn_recurrence.restype = ctypes.c_int
         lib.nvfp4_status_string.argtypes = [ctypes.c_int]
         lib.nvfp4_status_string.restype = ctypes.c_char_p
         lib.nvfp4_version.argtypes = []
@@ -278,6 +289,31 @@ def nvfp4_harmonize_scales(w: NVFP4Tensor, seg_offsets, seg_global_scales: torch
     _check(st, "nvfp4_harmonize_scales")
 
 
+def nvfp4_gdn_workspace_bytes(tokens: int, v_heads: int) -> int:
+    return int(load().nvfp4_gdn_workspace_bytes(tokens, v_heads))
+
+
+def nvfp4_gdn_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor, g: torch.Tensor,
+                         o: torch.Tensor, k_heads: int, v_heads: int, workspace: torch.Tensor,
+                         normalize_qk: bool = True, s0: torch.Tensor | None = None,
+                         s_final: torch.Tensor | None = None, stream=None) -> None:
+    """C ``nvfp4_gdn_recurrence`` on 2-D row-strided views (one dtype for the
+    inputs; they may be column slices of one fused in-projection output)."""
+    for t in (q, k, v, beta, g, o):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise NVFP4Error("inputs and output must be 2-D with contiguous rows")
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k, v, beta, g)):
+        raise NVFP4Error("q, k, v, beta and g must share one dtype")
+    ins = _GdnInputs(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), v.data_ptr(), v.stride(0),
+                     beta.data_ptr(), beta.stride(0), g.data_ptr(), g.stride(0))
+    st = load().nvfp4_gdn_recurrence(ctypes.byref(ins), dt, q.shape[0], k_heads, v_heads, int(normalize_qk),
+                                     _ptr(s0), _ptr(s_final), o.data_ptr(), _dtype_code(o), o.stride(0),
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream(q.device, stream))
+    _check(st, "nvfp4_gdn_recurrence")
+
+
 # ----------------------------------------------------------- conveniences
 
 def quantize(x: torch.Tensor, static_scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
@@ -362,3 +398,15 @@ def harmonize_scales(w: NVFP4Tensor, seg_offsets, seg_global_scales: torch.Tenso
     g = torch.empty(1, dtype=torch.float32, device=w.codes.device)
     nvfp4_harmonize_scales(w, seg_offsets, seg_global_scales, scales, g)
     return NVFP4Tensor(w.codes, scales, g, w.rows, w.cols)
+
+
+def gdn_recurrence(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor, g: torch.Tensor,
+                   k_heads: int, v_heads: int, normalize_qk: bool = True, s0: torch.Tensor | None = None,
+                   out_dtype=torch.float32, return_state: bool = False):
+    """Outputs [tokens, v_heads*128] (and the final states [v_heads, 128, 128])."""
+    tokens = q.shape[0]
+    ws = torch.empty(nvfp4_gdn_workspace_bytes(tokens, v_heads) // 4, dtype=torch.float32, device=q.device)
+    o = torch.empty((tokens, v_heads * 128), dtype=out_dtype, device=q.device)
+    sf = torch.empty((v_heads, 128, 128), dtype=torch.float32, device=q.device) if return_state else None
+    nvfp4_gdn_recurrence(q, k, v, beta, g, o, k_heads, v_heads, ws, normalize_qk, s0, sf)
+    return (o, sf) if return_state else o

@@ -300,6 +300,56 @@ int nvfp4_harmonize_scales(const nvfp4_tensor* w, int n_segments, const int64_t*
                                      (hipStream_t)stream));
 }
 
+size_t nvfp4_gdn_workspace_bytes(int64_t tokens, int v_heads) {
+  if (tokens <= 0 || v_heads <= 0) return 0;
+  return sizeof(float) * gdn_workspace_floats(tokens, v_heads);
+}
+
+int nvfp4_gdn_recurrence(const nvfp4_gdn_inputs* in, int in_dtype, int64_t tokens, int k_heads,
+                         int v_heads, int normalize_qk, const float* s0, float* s_final, void* o,
+                         int o_dtype, int64_t ld_o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (in == nullptr || in->q == nullptr || in->k == nullptr || in->v == nullptr ||
+      in->beta == nullptr || in->g == nullptr || o == nullptr || workspace == nullptr)
+    return NVFP4_ERR_NULL;
+  if (in_dtype != NVFP4_DTYPE_BF16 && in_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (o_dtype != NVFP4_DTYPE_BF16 && o_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (tokens <= 0 || k_heads <= 0 || v_heads <= 0 || v_heads % k_heads != 0 || v_heads > 4096)
+    return NVFP4_ERR_SHAPE;
+  if (tokens >= kIndexLimit) return NVFP4_ERR_RANGE;
+  const int64_t kw = (int64_t)k_heads * 128, vw = (int64_t)v_heads * 128;
+  if (in->ld_q < kw || in->ld_k < kw || in->ld_v < vw || in->ld_beta < v_heads || in->ld_g < v_heads ||
+      ld_o < vw)
+    return NVFP4_ERR_STRIDE;
+  const uintptr_t ea = in_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if ((in->ld_q * (int64_t)ea) % 16 != 0 || (in->ld_k * (int64_t)ea) % 16 != 0 ||
+      (in->ld_v * (int64_t)ea) % 16 != 0)
+    return NVFP4_ERR_STRIDE;  // q, k, v rows are read with 16-byte loads
+  if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->v, 16) || !aligned(in->beta, ea) ||
+      !aligned(in->g, ea) || !aligned(o, o_dtype == NVFP4_DTYPE_BF16 ? 2 : 4) || !aligned(workspace, 16) ||
+      !aligned(s0, 4) || !aligned(s_final, 4))
+    return NVFP4_ERR_ALIGN;
+  if (workspace_bytes < nvfp4_gdn_workspace_bytes(tokens, v_heads)) return NVFP4_ERR_WORKSPACE;
+  GdnArgs p{};
+  p.q = in->q; p.ld_q = in->ld_q;
+  p.k = in->k; p.ld_k = in->ld_k;
+  p.v = in->v; p.ld_v = in->ld_v;
+  p.beta = in->beta; p.ld_beta = in->ld_beta;
+  p.g = in->g; p.ld_g = in->ld_g;
+  p.in_dtype = in_dtype;
+  p.T = tokens;
+  p.hk = k_heads;
+  p.hv = v_heads;
+  p.n_chunks = (int)((tokens + 63) / 64);
+  p.normalize = normalize_qk != 0;
+  p.s0 = s0;
+  p.s_final = s_final;
+  p.o = o;
+  p.ld_o = ld_o;
+  p.o_dtype = o_dtype;
+  return hip_status(launch_gdn(p, (float*)workspace, (hipStream_t)stream));
+}
+
 const char* nvfp4_status_string(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

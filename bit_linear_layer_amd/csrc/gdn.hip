@@ -1,0 +1,413 @@
+// Gated delta-rule recurrence of a Gated DeltaNet layer, consuming the gate
+// epilogue's write strength beta = sigmoid(b) and log-space decay
+// g = -exp(A_log) softplus(a + dt_bias) (chatpaper.ai English abstract,
+// mechanisms (ii) and (iii); evolve.pub review, "Key claims under review",
+// third claim).  Per value head, state S in R^{128 x 128} (rows: value dims,
+// columns: key dims):
+//     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+//     o_t = S_t q_t,
+// the published gated delta rule; q/k heads are shared by groups of value
+// heads, optionally L2-normalized (q scaled by 128^-1/2).  float32 throughout.
+//
+// Chunked form (64 tokens per chunk, derived from the update): with
+// u_t = beta_t (v_t - exp(g_t) S_{t-1} k_t) the update is
+// S_t = exp(g_t) S_{t-1} + u_t k_t^T.  Inside a chunk starting from S0 with
+// cumulative decay G_t = exp(g_1 + ... + g_t):
+//     (I + M) U = diag(beta) (V - diag(G) K S0^T),
+//     M[t][j] = beta_t (G_t / G_j) k_t.k_j  (j < t),
+// so U = Ut - Wt S0^T with [Wt | Ut] = (I + M)^-1 diag(beta) [diag(G) K | V];
+//     O = diag(G) Q S0^T + A U,  A[t][j] = (G_t / G_j) q_t.k_j  (j <= t),
+//     S_end = G_C S0 + U^T diag(G_C / G) K.
+// Wt, Ut, A, diag(G) Q and diag(G_C/G) K depend on the chunk only, so one
+// kernel computes them for every (head, chunk) in parallel; a second walks
+// the chunks in order per (head, 32-row slice of S): the rows of S evolve
+// independently, so slices need no communication.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+using namespace dev;
+
+constexpr int kD = 128;   // head dimension (keys and values)
+constexpr int kC = 64;    // tokens per chunk
+constexpr int kSlice = 32;  // state rows per scan workgroup
+constexpr int kThreads = 256;       // prep workgroup
+constexpr int kScanThreads = 512;   // scan workgroup
+// LDS row strides, padded so the 16 rows a wave reads at once fall into
+// distinct banks (an unpadded 512-byte stride puts them all in one)
+constexpr int kP = kD + 4;   // rows of 128 floats
+constexpr int kPA = kC + 4;  // rows of 64 floats
+
+// Workspace per (value head, chunk), floats.
+constexpr int64_t kWsW = 0;                  // Wt   [64][128]
+constexpr int64_t kWsU = kWsW + kC * kD;     // Ut   [64][128]
+constexpr int64_t kWsA = kWsU + kC * kD;     // A    [64][64]
+constexpr int64_t kWsQ = kWsA + kC * kC;     // diag(G) Q        [64][128]
+constexpr int64_t kWsK = kWsQ + kC * kD;     // diag(G_C / G) K  [64][128]
+constexpr int64_t kWsG = kWsK + kC * kD;     // G_C (one float, padded to 4)
+constexpr int64_t kWsPerChunk = kWsG + 4;
+
+template <int DT>
+__device__ inline float load_elem(const void* base, int64_t idx) {
+  if constexpr (DT == NVFP4_DTYPE_BF16) {
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[idx] << 16);
+  } else {
+    return reinterpret_cast<const float*>(base)[idx];
+  }
+}
+
+// 32 consecutive elements (a quarter of a 128-wide head row) as floats, with
+// 16-byte loads (rows are 16-byte aligned); zeros when !valid.
+template <int DT>
+__device__ inline void load32(const void* base, int64_t elem, bool valid, float v[32]) {
+  if constexpr (DT == NVFP4_DTYPE_BF16) {
+    uint4 w[4];
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    if (valid) {  // rows past the end are never read
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = src[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * j + 2 * e] = __uint_as_float(x[e] << 16);
+        v[8 * j + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+    float4 f[8];
+    if (valid) {  // rows past the end are never read
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = src[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[4 * j] = f[j].x; v[4 * j + 1] = f[j].y; v[4 * j + 2] = f[j].z; v[4 * j + 3] = f[j].w;
+    }
+  }
+}
+
+__device__ inline void store32(float* dst, const float v[32]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    reinterpret_cast<float4*>(dst)[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+}
+
+// Inclusive prefix sum over the 64 lanes of one wave.
+__device__ inline float wave_prefix_sum(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gdn_prep_kernel(GdnArgs p, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float sk[kC][kP];  // k rows (normalized)
+  __shared__ __attribute__((aligned(16))) float sq[kC][kP];  // q rows (normalized, scaled)
+  __shared__ __attribute__((aligned(16))) float sm[kC][kPA];  // M (strictly lower)
+  __shared__ float sgam[kC];     // cumulative log decay
+  __shared__ float sbeta[kC];
+
+  const int chunk = blockIdx.x, h = blockIdx.y;
+  const int hk = h / (p.hv / p.hk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)chunk * kC;
+  float* out = ws + ((int64_t)h * p.n_chunks + chunk) * kWsPerChunk;
+
+  // q, k rows of the chunk (zero beyond T: such tokens have beta = 0, g = 0
+  // and leave the state unchanged); thread -> row tid/4, quarter tid%4, all
+  // loads issued before use; L2 norms reduced over the row's 4 threads
+  {
+    const int t = tid >> 2, part = tid & 3;
+    const int64_t tt = t0 + t;
+    const bool valid = tt < p.T;
+    float kr[32], qr[32];
+    load32<DT>(p.k, tt * p.ld_k + (int64_t)hk * kD + part * 32, valid, kr);
+    load32<DT>(p.q, tt * p.ld_q + (int64_t)hk * kD + part * 32, valid, qr);
+    if (p.normalize) {
+      float sk2 = 0.0f, sq2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        sk2 += kr[e] * kr[e];
+        sq2 += qr[e] * qr[e];
+      }
+      sk2 += __shfl_xor(sk2, 1);
+      sk2 += __shfl_xor(sk2, 2);
+      sq2 += __shfl_xor(sq2, 1);
+      sq2 += __shfl_xor(sq2, 2);
+      const float ik = 1.0f / fmaxf(sqrtf(sk2), 1e-30f);
+      const float iq = 0.08838834764831845f / fmaxf(sqrtf(sq2), 1e-30f);  // 128^-1/2 / |q|
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        kr[e] *= ik;
+        qr[e] *= iq;
+      }
+    }
+    store32(&sk[t][part * 32], kr);
+    store32(&sq[t][part * 32], qr);
+  }
+  if (wave == 0) {
+    const int64_t tt = t0 + lane;
+    float b = 0.0f, g = 0.0f;
+    if (tt < p.T) {
+      b = load_elem<DT>(p.beta, tt * p.ld_beta + h);
+      g = load_elem<DT>(p.g, tt * p.ld_g + h);
+    }
+    sbeta[lane] = b;
+    sgam[lane] = wave_prefix_sum(g, lane);
+  }
+  __syncthreads();
+
+  // M[t][j] = beta_t exp(gam_t - gam_j) k_t.k_j (j < t) and
+  // A[t][j] = exp(gam_t - gam_j) q_t.k_j (j <= t): thread -> row t, 16 columns
+  {
+    const int t = tid >> 2, j0 = (tid & 3) * 16;
+    float km[16], qm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) km[i] = qm[i] = 0.0f;
+    for (int d = 0; d < kD; d += 4) {
+      const float4 kt = *reinterpret_cast<const float4*>(&sk[t][d]);
+      const float4 qt = *reinterpret_cast<const float4*>(&sq[t][d]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 kj = *reinterpret_cast<const float4*>(&sk[j0 + i][d]);
+        km[i] += kt.x * kj.x + kt.y * kj.y + kt.z * kj.z + kt.w * kj.w;
+        qm[i] += qt.x * kj.x + qt.y * kj.y + qt.z * kj.z + qt.w * kj.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = j0 + i;
+      const float dec = expf(sgam[t] - sgam[j]);
+      sm[t][j] = j < t ? sbeta[t] * dec * km[i] : 0.0f;
+      out[kWsA + t * kC + j] = j <= t ? dec * qm[i] : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // diag(G) Q goes out now: the q rows' LDS then holds the chunk's v rows
+  for (int i = tid; i < kC * kD; i += kThreads) out[kWsQ + i] = expf(sgam[i / kD]) * sq[i / kD][i % kD];
+  __syncthreads();
+  {
+    const int t = tid >> 2, part = tid & 3;
+    float vr[32];
+    load32<DT>(p.v, (t0 + t) * p.ld_v + (int64_t)h * kD + part * 32, t0 + t < p.T, vr);
+    store32(&sq[t][part * 32], vr);
+  }
+  __syncthreads();
+
+  // diag(G_C / G) K and G_C go out before the k rows are overwritten
+  const float gc = sgam[kC - 1];
+  for (int i = tid; i < kC * kD; i += kThreads) out[kWsK + i] = expf(gc - sgam[i / kD]) * sk[i / kD][i % kD];
+  if (tid == 0) out[kWsG] = expf(gc);
+  __syncthreads();  // every read of the k rows is done before they are overwritten
+
+  // [Wt | Ut] = (I + M)^-1 diag(beta) [diag(G) K | V] by forward substitution
+  // in place: thread c owns column c of [k rows | v rows] (a wave's columns
+  // are all of one kind); 16 rows at a time in registers, earlier rows read
+  // back final from LDS, M read as a broadcast.
+  {
+    const bool wcol = tid < kD;
+    const int cc = tid & (kD - 1);
+    float* col = wcol ? &sk[0][cc] : &sq[0][cc];  // element t at col[t * kP]
+    for (int t = 0; t < kC; ++t) col[t * kP] *= sbeta[t] * (wcol ? expf(sgam[t]) : 1.0f);
+    for (int b0 = 0; b0 < kC; b0 += 16) {
+      float r[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) r[i] = col[(b0 + i) * kP];
+      for (int j = 0; j < b0; j += 4) {  // b0 is a multiple of 16
+        const float y0 = col[j * kP], y1 = col[(j + 1) * kP], y2 = col[(j + 2) * kP], y3 = col[(j + 3) * kP];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float4 m = *reinterpret_cast<const float4*>(&sm[b0 + i][j]);
+          r[i] -= m.x * y0 + m.y * y1 + m.z * y2 + m.w * y3;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < i; ++jj) r[i] -= sm[b0 + i][b0 + jj] * r[jj];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) col[(b0 + i) * kP] = r[i];
+    }
+    float* dst = out + (wcol ? kWsW : kWsU);
+    for (int t = 0; t < kC; ++t) dst[t * kD + cc] = col[t * kP];
+  }
+}
+
+// One workgroup per (value head, 32-row slice of S); chunks in order.  The
+// next chunk's data is loaded into registers while the current one is
+// computed.
+struct ChunkRegs {
+  float4 w[4], q[4], k[4], a[2], u;
+  float gc;
+};
+
+__device__ inline void load_chunk(const float* in, int tid, int row0, ChunkRegs& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.w[i] = reinterpret_cast<const float4*>(in + kWsW)[tid + i * kScanThreads];
+    r.q[i] = reinterpret_cast<const float4*>(in + kWsQ)[tid + i * kScanThreads];
+    r.k[i] = reinterpret_cast<const float4*>(in + kWsK)[tid + i * kScanThreads];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) r.a[i] = reinterpret_cast<const float4*>(in + kWsA)[tid + i * kScanThreads];
+  r.u = *reinterpret_cast<const float4*>(in + kWsU + (tid >> 3) * kD + row0 + (tid & 7) * 4);
+  r.gc = in[kWsG];
+}
+
+template <int ODT>
+__global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float sS[kSlice][kP];  // this slice of the state
+  __shared__ __attribute__((aligned(16))) float sW[kC][kP];      // Wt
+  __shared__ __attribute__((aligned(16))) float sQ[kC][kP];      // diag(G) Q
+  __shared__ __attribute__((aligned(16))) float sK[kC][kP];      // diag(G_C/G) K
+  __shared__ __attribute__((aligned(16))) float sA[kC][kPA];
+  __shared__ __attribute__((aligned(16))) float sU[kC][kSlice + 4];
+
+  // workgroups of one head on one XCD (ids are dealt to the 8 XCDs
+  // round-robin), so its slices share the L2 copy of the chunk data
+  constexpr int nsl = kD / kSlice;
+  const int bid = blockIdx.x;
+  const int x = bid % 8, r8 = bid / 8;
+  const int h = (r8 / nsl) * 8 + x, sl = r8 % nsl;
+  if (h >= p.hv) return;
+  const int tid = threadIdx.x;
+  const int row0 = sl * kSlice;
+  const float* base = ws + (int64_t)h * p.n_chunks * kWsPerChunk;
+
+  auto store_chunk = [&](const ChunkRegs& r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = tid + i * kScanThreads;  // float4 index in a [64][128] block
+      const int rr = f / (kD / 4), cc = (f % (kD / 4)) * 4;
+      *reinterpret_cast<float4*>(&sW[rr][cc]) = r.w[i];
+      *reinterpret_cast<float4*>(&sQ[rr][cc]) = r.q[i];
+      *reinterpret_cast<float4*>(&sK[rr][cc]) = r.k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int f = tid + i * kScanThreads;  // float4 index in a [64][64] block
+      *reinterpret_cast<float4*>(&sA[f / (kC / 4)][(f % (kC / 4)) * 4]) = r.a[i];
+    }
+  };
+
+  for (int i = tid; i < kSlice * kD; i += kScanThreads) {
+    const int c = i / kD, d = i % kD;
+    sS[c][d] = p.s0 != nullptr ? p.s0[((int64_t)h * kD + row0 + c) * kD + d] : 0.0f;
+  }
+  ChunkRegs cur, nxt;
+  load_chunk(base, tid, row0, cur);
+  store_chunk(cur);
+  __syncthreads();
+
+  const int t = tid >> 3, c0 = (tid & 7) * 4;  // U / O outputs: row t, 4 slice columns
+  for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
+    if (chunk + 1 < p.n_chunks) load_chunk(base + (int64_t)(chunk + 1) * kWsPerChunk, tid, row0, nxt);
+
+    // U = Ut - Wt S^T and the first half of O = diag(G) Q S^T
+    float u[4] = {cur.u.x, cur.u.y, cur.u.z, cur.u.w}, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int d = 0; d < kD; d += 4) {
+      const float4 w = *reinterpret_cast<const float4*>(&sW[t][d]);
+      const float4 q = *reinterpret_cast<const float4*>(&sQ[t][d]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 sv = *reinterpret_cast<const float4*>(&sS[c0 + i][d]);
+        u[i] -= w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
+        o[i] += q.x * sv.x + q.y * sv.y + q.z * sv.z + q.w * sv.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sU[t][c0 + i] = u[i];
+    __syncthreads();
+    // O += A U (A is lower triangular)
+    for (int j = 0; j <= t; ++j) {
+      const float a = sA[t][j];
+      const float4 uj = *reinterpret_cast<const float4*>(&sU[j][c0]);
+      o[0] += a * uj.x; o[1] += a * uj.y; o[2] += a * uj.z; o[3] += a * uj.w;
+    }
+    const int64_t tt = (int64_t)chunk * kC + t;
+    if (tt < p.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t idx = tt * p.ld_o + (int64_t)h * kD + row0 + c0 + i;
+        if constexpr (ODT == NVFP4_DTYPE_BF16)
+          reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)f32_to_bf16_bits(o[i]);
+        else
+          reinterpret_cast<float*>(p.o)[idx] = o[i];
+      }
+    }
+    // S = G_C S + U^T diag(G_C/G) K: thread -> row c = tid / 16, 8 key dims
+    {
+      const int c = tid >> 4, d0 = (tid & 15) * 8;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = cur.gc * sS[c][d0 + e];
+      for (int j = 0; j < kC; ++j) {
+        const float uj = sU[j][c];
+        const float4 k0 = *reinterpret_cast<const float4*>(&sK[j][d0]);
+        const float4 k1 = *reinterpret_cast<const float4*>(&sK[j][d0 + 4]);
+        acc[0] += uj * k0.x; acc[1] += uj * k0.y; acc[2] += uj * k0.z; acc[3] += uj * k0.w;
+        acc[4] += uj * k1.x; acc[5] += uj * k1.y; acc[6] += uj * k1.z; acc[7] += uj * k1.w;
+      }
+      __syncthreads();  // every read of the old slice (and of this chunk's data) is done
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sS[c][d0 + e] = acc[e];
+    }
+    if (chunk + 1 < p.n_chunks) {
+      store_chunk(nxt);
+      cur = nxt;
+    }
+    __syncthreads();
+  }
+  if (p.s_final != nullptr)
+    for (int i = tid; i < kSlice * kD; i += kScanThreads) {
+      const int c = i / kD, d = i % kD;
+      p.s_final[((int64_t)h * kD + row0 + c) * kD + d] = sS[c][d];
+    }
+}
+
+}  // namespace
+
+size_t gdn_workspace_floats(int64_t T, int hv) {
+  const int64_t chunks = (T + kC - 1) / kC;
+  return (size_t)(chunks * hv * kWsPerChunk);
+}
+
+hipError_t launch_gdn(const GdnArgs& p, float* ws, hipStream_t s) {
+  const dim3 prep((unsigned)p.n_chunks, (unsigned)p.hv);
+  if (p.in_dtype == NVFP4_DTYPE_BF16)
+    gdn_prep_kernel<NVFP4_DTYPE_BF16><<<prep, kThreads, 0, s>>>(p, ws);
+  else
+    gdn_prep_kernel<NVFP4_DTYPE_F32><<<prep, kThreads, 0, s>>>(p, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nsl = kD / kSlice;
+  const unsigned blocks = (unsigned)(((p.hv + 7) / 8) * 8 * nsl);
+  if (p.o_dtype == NVFP4_DTYPE_BF16)
+    gdn_scan_kernel<NVFP4_DTYPE_BF16><<<blocks, kScanThreads, 0, s>>>(p, ws);
+  else
+    gdn_scan_kernel<NVFP4_DTYPE_F32><<<blocks, kScanThreads, 0, s>>>(p, ws);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

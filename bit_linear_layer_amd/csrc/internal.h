@@ -94,4 +94,21 @@ hipError_t launch_harmonize(const uint8_t* in, int64_t ld_in, uint8_t* out, int6
 bool skinny_eligible(const GemmArgs& p);
 hipError_t launch_gemm_skinny(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s);
 
+// Gated delta-rule recurrence (gdn.hip).
+struct GdnArgs {
+  const void* q; int64_t ld_q;
+  const void* k; int64_t ld_k;
+  const void* v; int64_t ld_v;
+  const void* beta; int64_t ld_beta;
+  const void* g; int64_t ld_g;
+  int in_dtype;
+  int64_t T;
+  int hk, hv, n_chunks, normalize;
+  const float* s0;
+  float* s_final;
+  void* o; int64_t ld_o; int o_dtype;
+};
+size_t gdn_workspace_floats(int64_t T, int hv);
+hipError_t launch_gdn(const GdnArgs& p, float* ws, hipStream_t s);
+
 }  // namespace nvfp4

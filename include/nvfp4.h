@@ -274,6 +274,53 @@ int nvfp4_harmonize_scales(const nvfp4_tensor* w, int n_segments, const int64_t*
                            const float* seg_global_scales, uint8_t* out_scales,
                            int64_t ld_out_scales, float* out_global_scale, void* stream);
 
+/*
+ * Gated delta-rule recurrence of a Gated DeltaNet layer (chatpaper.ai
+ * English abstract, mechanisms (ii) and (iii); evolve.pub review, "Key
+ * claims under review", third claim), consuming the gate epilogue's outputs
+ * beta = sigmoid(b) and the log-space decay g.  The published update, per
+ * value head h with a float32 state S in R^{128 x 128}:
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t.
+ * Heads are 128 wide.  Value head h reads q/k head h / (v_heads / k_heads).
+ * With normalize_qk != 0, q and k are L2-normalized per head and q is scaled
+ * by 128^-1/2 first (the short convolution of a GDN layer is not part of
+ * this call).  Computed in float32, chunk-parallel (64 tokens per chunk).
+ *
+ * Each input is a row-major [tokens, width] matrix given by a device pointer
+ * and a row stride in elements, all of one dtype (bf16 or float32), so the
+ * columns of a fused in-projection output can be passed directly:
+ *   q, k   [tokens, k_heads * 128];  v  [tokens, v_heads * 128];
+ *   beta, g [tokens, v_heads].
+ * q, k and v rows start on 16-byte boundaries (pointer and row stride).
+ */
+typedef struct {
+  const void* q; int64_t ld_q;
+  const void* k; int64_t ld_k;
+  const void* v; int64_t ld_v;
+  const void* beta; int64_t ld_beta;
+  const void* g; int64_t ld_g;
+} nvfp4_gdn_inputs;
+
+/* Bytes of device workspace nvfp4_gdn_recurrence needs (per-chunk data,
+ * about 144 KB per value head and 64 tokens). */
+size_t nvfp4_gdn_workspace_bytes(int64_t tokens, int v_heads);
+
+/*
+ * nvfp4_gdn_recurrence -- o[t, h*128 + i] = (S_t q_t)[i] for every token t
+ * and value head h.
+ *   s0       DEVICE float32 [v_heads, 128, 128] initial states, or NULL (zeros).
+ *   s_final  DEVICE float32 [v_heads, 128, 128] receives the last states, or NULL.
+ *   o        DEVICE [tokens, ld_o] (bf16 or float32), ld_o >= v_heads * 128.
+ *   workspace DEVICE, >= nvfp4_gdn_workspace_bytes(tokens, v_heads) bytes,
+ *            16-byte aligned.
+ * 1 <= k_heads, v_heads % k_heads == 0, v_heads <= 4096.
+ */
+int nvfp4_gdn_recurrence(const nvfp4_gdn_inputs* in, int in_dtype, int64_t tokens, int k_heads,
+                         int v_heads, int normalize_qk, const float* s0, float* s_final, void* o,
+                         int o_dtype, int64_t ld_o, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Human-readable text of a status (and of the last HIP error, for NVFP4_ERR_HIP). */
 const char* nvfp4_status_string(int status);
 

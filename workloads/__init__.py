@@ -119,6 +119,33 @@ def gdn_in_proj(seed: int = 0, m: int = 32768, k: int = 5120, scale_rows: float 
                            "b_segment": 4, "a_segment": 5})
 
 
+def gdn_layer(seed: int = 0, m: int = 32768, k: int = 5120) -> Workload:
+    """The in-projection of one GDN layer for the recurrence study: X and the
+    q/k/v/z segments as gdn_in_proj, the b and a segments scaled to the
+    rows' RMS norm so that b ~ N(0, 1) and a ~ N(0, 0.25), A_log = ln U(1, 16)
+    and dt_bias = inverse softplus of dt with exp(A_log) * dt = 1 / horizon,
+    horizon ~ U(44000, 62000) tokens per head (the range of decay-gate
+    horizons the pages report)."""
+    rng = np.random.default_rng(seed)
+    x = heavy_x(rng, m, k)
+    xn = float(np.sqrt(np.mean(np.sum(x.astype(np.float64) ** 2, axis=1))))
+    segs = []
+    for name, rows, sigma in GDN_SEGMENTS:
+        if name == "b":
+            sigma = 1.0 / xn
+        elif name == "a":
+            sigma = 0.5 / xn
+        segs.append((name, to_bf16(normal_weight(rng, rows, k, sigma))))
+    heads = 48
+    a_log = np.log(rng.uniform(1.0, 16.0, size=heads))
+    horizon = rng.uniform(44000.0, 62000.0, size=heads)
+    dt = 1.0 / (np.exp(a_log) * horizon)
+    dt_bias = np.log(np.expm1(dt)).astype(np.float32)
+    return Workload(f"gdn_layer_m{m}_k{k}", to_bf16(x), segs,
+                    extra={"A_log": torch.from_numpy(a_log.astype(np.float32)),
+                           "dt_bias": torch.from_numpy(dt_bias), "b_segment": 4, "a_segment": 5})
+
+
 def mlp_pair(seed: int = 0, m: int = 8192, k: int = 5120, inter: int = 17408) -> Workload:
     """MLP pair: gate_up W [2*inter, k] as two segments (gate, up), then
     down W [k, inter]; all ~N(0, 0.02); heavy-tailed X."""
