@@ -250,6 +250,53 @@ struct TailLoader {
   }
 };
 
+// Row stride (bytes) of a bf16 output tile staged in LDS: 16 bytes of
+// padding move rows 4 apart (one MFMA lane group) off each other's banks.
+template <int COLS>
+constexpr int staged_row_bytes() { return COLS * 2 + 16; }
+
+// Copy a staged bf16 tile [rows][cols] to global memory, 16 bytes per lane,
+// rows at m0 (< M), columns at n0 (< n_hi); row starts 16-byte aligned.
+template <int ROWS, int COLS, int THREADS>
+__device__ inline void store_staged_tile(const uint8_t* tile, int m0, int n0, int M, int n_hi, uint16_t* out,
+                                         int64_t ld_out) {
+  constexpr int kChunksPerRow = COLS / 8;
+  for (int c = (int)threadIdx.x; c < ROWS * kChunksPerRow; c += THREADS) {
+    const int row = c / kChunksPerRow, col = (c % kChunksPerRow) * 8;
+    const int m = m0 + row, n = n0 + col;
+    if (m >= M || n >= n_hi) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(tile + row * staged_row_bytes<COLS>() + col * 2);
+    uint16_t* dst = out + (int64_t)m * ld_out + n;
+    if (n + 8 <= n_hi) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int q = 0; q < 8 && n + q < n_hi; ++q) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+    }
+  }
+}
+
+// The tile's scaled accumulators as bf16 into LDS, then coalesced stores.
+template <class C>
+__device__ __attribute__((always_inline)) inline void stage_bf16_and_store(
+    floatx16 (&acc)[C::FM][C::FN], int fm0, int fn0, int lane, uint8_t* smem, int m0, int n0, int M,
+    int n_hi, uint16_t* out, int64_t ld_out) {
+  constexpr int kRow = staged_row_bytes<C::BN>();
+  barrier_lds();  // every wave is done reading the K tiles' stages
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ml = (fm0 + i) * 32 + 4 * (lane >> 5) + 8 * (r >> 2) + (r & 3);
+        const int nl = (fn0 + j) * 32 + (lane & 31);
+        *reinterpret_cast<uint16_t*>(smem + ml * kRow + nl * 2) = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+      }
+  barrier_lds();
+  store_staged_tile<C::BM, C::BN, C::kThreads>(smem, m0, n0, M, n_hi, out, ld_out);
+}
+
 // Gated-MLP epilogue.  Lane (row, h column) holds the gate accumulator in
 // fragment j and the up accumulator in fragment j + FN/2.  Each is scaled and
 // rounded to bf16 exactly as the plain epilogue stores it, then
@@ -269,8 +316,8 @@ __device__ __attribute__((always_inline)) inline void swiglu_epilogue(
   const float ga = *p.ep.a_g;
   const float sg = ga * p.ep.seg_g[0], su = ga * p.ep.seg_g[1];
   const bool quant = p.ep.hq_codes != nullptr;
-  uint16_t* th = reinterpret_cast<uint16_t*>(smem);  // [BM][kHCols] bf16 h
-  if (quant) barrier_lds();  // every wave is done reading the last K tile
+  constexpr int kRow = staged_row_bytes<kHCols>();
+  barrier_lds();  // every wave is done reading the last K tile
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
@@ -286,11 +333,8 @@ __device__ __attribute__((always_inline)) inline void swiglu_epilogue(
         const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][r] * sg));
         const float u = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + FH][r] * su));
         const uint32_t hb = f32_to_bf16_bits(silu(g) * u);
-        if (m < p.M && hcol < p.ep.inter) {
-          amax = fmaxf(amax, __uint_as_float((hb & 0x7FFFu) << 16));
-          if (p.ep.h != nullptr) p.ep.h[(int64_t)m * p.ep.ld_h + hcol] = (uint16_t)hb;
-        }
-        if (quant) th[mloc * kHCols + hl] = (uint16_t)hb;
+        if (m < p.M && hcol < p.ep.inter) amax = fmaxf(amax, __uint_as_float((hb & 0x7FFFu) << 16));
+        *reinterpret_cast<uint16_t*>(smem + mloc * kRow + hl * 2) = (uint16_t)hb;
       }
     }
   }
@@ -300,15 +344,17 @@ __device__ __attribute__((always_inline)) inline void swiglu_epilogue(
       atomicMax(reinterpret_cast<unsigned int*>(p.ep.partials) + blockIdx.x % p.ep.n_partials,
                 __float_as_uint(amax));
   }
+  barrier_lds();
+  if (p.ep.h != nullptr)
+    store_staged_tile<C::BM, kHCols, C::kThreads>(smem, m0, n0, p.M, p.ep.inter, p.ep.h, p.ep.ld_h);
   if (quant) {
-    barrier_lds();
     const float gh = *p.ep.hq_g;
     constexpr int kBlocksPerRow = kHCols / 16;
     for (int b = (int)threadIdx.x; b < C::BM * kBlocksPerRow; b += C::kThreads) {
       const int mloc = b / kBlocksPerRow, jb = b % kBlocksPerRow;
       const int m = m0 + mloc, h0 = n0 + jb * 16;
       if (m >= p.M || h0 >= p.ep.inter) continue;  // inter % 16 == 0: blocks are whole
-      const uint16_t* src = th + mloc * kHCols + jb * 16;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(smem + mloc * kRow + jb * 32);
       const uint4 q0 = *reinterpret_cast<const uint4*>(src);
       const uint4 q1 = *reinterpret_cast<const uint4*>(src + 8);
       const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
@@ -498,6 +544,14 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
           acc[i][j][r] = x;
         }
       }
+  // bf16 output through LDS: the MFMA layout gives each lane one column of
+  // 16 rows, so direct stores are 2-byte scatters (one instruction per
+  // element); staged, every lane stores 16 contiguous bytes.
+  if (p.out_bf16 && p.ld_out % 8 == 0 && ((uintptr_t)p.out & 15) == 0 && n0 % 8 == 0) {
+    stage_bf16_and_store<C>(acc, fm0, fn0, lane, smem, m0, n0, p.M, n_hi,
+                            reinterpret_cast<uint16_t*>(p.out), p.ld_out);
+    return;
+  }
   const bool full_tile = m0 + C::BM <= p.M && n0 + C::BN <= n_hi;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
@@ -526,7 +580,9 @@ hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   constexpr int kCols = tile_cols<C, EPI>();
   const int tiles_n = (n_hi - n_lo + kCols - 1) / kCols;
   const int64_t nblocks = (int64_t)tiles_m * tiles_n;
-  const size_t lds = 3 * (size_t)C::kStage;  // three stages
+  // three K stages; the bf16 output tile is staged in the same memory afterwards
+  const size_t tile = (size_t)C::BM * staged_row_bytes<kCols>();
+  const size_t lds = 3 * (size_t)C::kStage > tile ? 3 * (size_t)C::kStage : tile;
   // raising the dynamic-LDS limit is idempotent and cheap
   hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C, EPI>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
