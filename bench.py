@@ -41,7 +41,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode / GDN measurements")
-    ap.add_argument("--cpu-rows", type=int, default=3072, help="rows of the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration) and exit")
     return ap.parse_args()
