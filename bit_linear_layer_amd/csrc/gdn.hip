@@ -33,6 +33,7 @@ namespace nvfp4 {
 namespace {
 
 using namespace dev;
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;   // head dimension (keys and values)
 constexpr int kC = 64;    // tokens per chunk
@@ -255,24 +256,35 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(GdnArgs p, float* __
 }
 
 // One workgroup per (value head, 32-row slice of S); chunks in order.  The
-// next chunk's data is loaded into registers while the current one is
-// computed.
-struct ChunkRegs {
-  float4 w[4], q[4], k[4], a[2], u;
-  float gc;
-};
+// three products of a chunk run on v_mfma_f32_16x16x4f32 (fp32 in, fp32
+// accumulate; lane l supplies A[l%16][l/16] and B[l/16][l%16] and holds
+// D[4(l/16)+r][l%16]):
+//   wave w: P = Wt S^T and O = diag(G) Q S^T for the 16x16 tile
+//           (t: 16(w/2).., c: 16(w%2)..), U = Ut - P, then O += A U;
+//   wave w: S[c][16w..16w+15] = G_C S + U^T diag(G_C/G) K for both 16-row
+//           halves of the slice.
+// The next chunk's data is loaded into registers while one is computed.
+constexpr int kPK = kD + 16;        // k rows, read down a column by 4 lane groups
+constexpr int kPU = kSlice + 16;    // U tile [64][32]
 
-__device__ inline void load_chunk(const float* in, int tid, int row0, ChunkRegs& r) {
+// A chunk's data in registers: thread tid holds 4-float group number
+// tid + 512 i of Wt, diag(G) Q, diag(G_C/G) K ([64][128]) and of A
+// ([64][64]), and the 4 elements of Ut its wave's U tile needs.  Native
+// vector types: arrays of HIP's float4 class stay in scratch memory.
+__device__ __attribute__((always_inline)) inline void scan_load(const float* in, int tid, int uoff, floatx4 (&w)[4],
+                                                                  floatx4 (&q)[4], floatx4 (&k)[4], floatx4 (&a)[2],
+                                                                  float (&u)[4], float& gc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r.w[i] = reinterpret_cast<const float4*>(in + kWsW)[tid + i * kScanThreads];
-    r.q[i] = reinterpret_cast<const float4*>(in + kWsQ)[tid + i * kScanThreads];
-    r.k[i] = reinterpret_cast<const float4*>(in + kWsK)[tid + i * kScanThreads];
+    w[i] = reinterpret_cast<const floatx4*>(in + kWsW)[tid + i * kScanThreads];
+    q[i] = reinterpret_cast<const floatx4*>(in + kWsQ)[tid + i * kScanThreads];
+    k[i] = reinterpret_cast<const floatx4*>(in + kWsK)[tid + i * kScanThreads];
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) r.a[i] = reinterpret_cast<const float4*>(in + kWsA)[tid + i * kScanThreads];
-  r.u = *reinterpret_cast<const float4*>(in + kWsU + (tid >> 3) * kD + row0 + (tid & 7) * 4);
-  r.gc = in[kWsG];
+  for (int i = 0; i < 2; ++i) a[i] = reinterpret_cast<const floatx4*>(in + kWsA)[tid + i * kScanThreads];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) u[r] = in[kWsU + uoff + r * kD];
+  gc = in[kWsG];
 }
 
 template <int ODT>
@@ -280,9 +292,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   __shared__ __attribute__((aligned(16))) float sS[kSlice][kP];  // this slice of the state
   __shared__ __attribute__((aligned(16))) float sW[kC][kP];      // Wt
   __shared__ __attribute__((aligned(16))) float sQ[kC][kP];      // diag(G) Q
-  __shared__ __attribute__((aligned(16))) float sK[kC][kP];      // diag(G_C/G) K
+  __shared__ __attribute__((aligned(16))) float sK[kC][kPK];     // diag(G_C/G) K
   __shared__ __attribute__((aligned(16))) float sA[kC][kPA];
-  __shared__ __attribute__((aligned(16))) float sU[kC][kSlice + 4];
+  __shared__ float sU[kC][kPU];
 
   // workgroups of one head on one XCD (ids are dealt to the 8 XCDs
   // round-robin), so its slices share the L2 copy of the chunk data
@@ -292,92 +304,91 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   const int h = (r8 / nsl) * 8 + x, sl = r8 % nsl;
   if (h >= p.hv) return;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  const int ti = wave >> 1, tj = wave & 1;  // U / O tile
   const int row0 = sl * kSlice;
   const float* base = ws + (int64_t)h * p.n_chunks * kWsPerChunk;
 
-  auto store_chunk = [&](const ChunkRegs& r) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int f = tid + i * kScanThreads;  // float4 index in a [64][128] block
-      const int rr = f / (kD / 4), cc = (f % (kD / 4)) * 4;
-      *reinterpret_cast<float4*>(&sW[rr][cc]) = r.w[i];
-      *reinterpret_cast<float4*>(&sQ[rr][cc]) = r.q[i];
-      *reinterpret_cast<float4*>(&sK[rr][cc]) = r.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int f = tid + i * kScanThreads;  // float4 index in a [64][64] block
-      *reinterpret_cast<float4*>(&sA[f / (kC / 4)][(f % (kC / 4)) * 4]) = r.a[i];
-    }
-  };
+  const int uoff = (16 * ti + 4 * lk) * kD + row0 + 16 * tj + li;  // this lane's Ut elements
+  floatx4 nw[4], nq[4], nk[4], na[2];
+  float nu[4], ngc;
+  float cu[4], cgc;
 
   for (int i = tid; i < kSlice * kD; i += kScanThreads) {
     const int c = i / kD, d = i % kD;
     sS[c][d] = p.s0 != nullptr ? p.s0[((int64_t)h * kD + row0 + c) * kD + d] : 0.0f;
   }
-  ChunkRegs cur, nxt;
-  load_chunk(base, tid, row0, cur);
-  store_chunk(cur);
-  __syncthreads();
+  scan_load(base, tid, uoff, nw, nq, nk, na, nu, ngc);
 
-  const int t = tid >> 3, c0 = (tid & 7) * 4;  // U / O outputs: row t, 4 slice columns
   for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
-    if (chunk + 1 < p.n_chunks) load_chunk(base + (int64_t)(chunk + 1) * kWsPerChunk, tid, row0, nxt);
+    // this chunk's data: registers -> LDS (every read of the previous
+    // chunk's data is behind the barrier at the end of the iteration)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = tid + i * kScanThreads;
+      const int rr = f / (kD / 4), cc = (f % (kD / 4)) * 4;
+      *reinterpret_cast<floatx4*>(&sW[rr][cc]) = nw[i];
+      *reinterpret_cast<floatx4*>(&sQ[rr][cc]) = nq[i];
+      *reinterpret_cast<floatx4*>(&sK[rr][cc]) = nk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int f = tid + i * kScanThreads;
+      *reinterpret_cast<floatx4*>(&sA[f / (kC / 4)][(f % (kC / 4)) * 4]) = na[i];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cu[r] = nu[r];
+    cgc = ngc;
+    __syncthreads();
+    // the next chunk's loads fly while this one is computed; unconditional
+    // (the last chunk reloads itself): a load under a branch makes the
+    // compiler wait for it where the paths join
+    scan_load(base + (int64_t)(chunk + 1 < p.n_chunks ? chunk + 1 : chunk) * kWsPerChunk, tid, uoff, nw, nq, nk, na,
+              nu, ngc);
 
-    // U = Ut - Wt S^T and the first half of O = diag(G) Q S^T
-    float u[4] = {cur.u.x, cur.u.y, cur.u.z, cur.u.w}, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int d = 0; d < kD; d += 4) {
-      const float4 w = *reinterpret_cast<const float4*>(&sW[t][d]);
-      const float4 q = *reinterpret_cast<const float4*>(&sQ[t][d]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 sv = *reinterpret_cast<const float4*>(&sS[c0 + i][d]);
-        u[i] -= w.x * sv.x + w.y * sv.y + w.z * sv.z + w.w * sv.w;
-        o[i] += q.x * sv.x + q.y * sv.y + q.z * sv.z + q.w * sv.w;
-      }
+    // P = Wt S^T and O = diag(G) Q S^T on this wave's tile
+    floatx4 accp = {0.0f, 0.0f, 0.0f, 0.0f}, acco = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int k = 0; k < kD / 4; ++k) {
+      const float bs = sS[16 * tj + li][4 * k + lk];
+      accp = __builtin_amdgcn_mfma_f32_16x16x4f32(sW[16 * ti + li][4 * k + lk], bs, accp, 0, 0, 0);
+      acco = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[16 * ti + li][4 * k + lk], bs, acco, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sU[t][c0 + i] = u[i];
+    for (int q = 0; q < 4; ++q) sU[16 * ti + 4 * lk + q][16 * tj + li] = cu[q] - accp[q];
     __syncthreads();
-    // O += A U (A is lower triangular)
-    for (int j = 0; j <= t; ++j) {
-      const float a = sA[t][j];
-      const float4 uj = *reinterpret_cast<const float4*>(&sU[j][c0]);
-      o[0] += a * uj.x; o[1] += a * uj.y; o[2] += a * uj.z; o[3] += a * uj.w;
-    }
-    const int64_t tt = (int64_t)chunk * kC + t;
-    if (tt < p.T) {
+    // O += A U over the key positions j <= t (A is lower triangular)
+    for (int k = 0; k < 4 * (ti + 1); ++k)
+      acco = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * ti + li][4 * k + lk], sU[4 * k + lk][16 * tj + li], acco,
+                                                  0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t idx = tt * p.ld_o + (int64_t)h * kD + row0 + c0 + i;
+    for (int q = 0; q < 4; ++q) {
+      const int64_t tt = (int64_t)chunk * kC + 16 * ti + 4 * lk + q;
+      if (tt < p.T) {
+        const int64_t idx = tt * p.ld_o + (int64_t)h * kD + row0 + 16 * tj + li;
         if constexpr (ODT == NVFP4_DTYPE_BF16)
-          reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)f32_to_bf16_bits(o[i]);
+          reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)f32_to_bf16_bits(acco[q]);
         else
-          reinterpret_cast<float*>(p.o)[idx] = o[i];
+          reinterpret_cast<float*>(p.o)[idx] = acco[q];
       }
     }
-    // S = G_C S + U^T diag(G_C/G) K: thread -> row c = tid / 16, 8 key dims
-    {
-      const int c = tid >> 4, d0 = (tid & 15) * 8;
-      float acc[8];
+    // S[c][16w + j] = G_C S + U^T diag(G_C/G) K: each wave reads and writes
+    // only its own 16 columns of the slice, after every wave's reads of S
+    // above (the barrier after U)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = cur.gc * sS[c][d0 + e];
-      for (int j = 0; j < kC; ++j) {
-        const float uj = sU[j][c];
-        const float4 k0 = *reinterpret_cast<const float4*>(&sK[j][d0]);
-        const float4 k1 = *reinterpret_cast<const float4*>(&sK[j][d0 + 4]);
-        acc[0] += uj * k0.x; acc[1] += uj * k0.y; acc[2] += uj * k0.z; acc[3] += uj * k0.w;
-        acc[4] += uj * k1.x; acc[5] += uj * k1.y; acc[6] += uj * k1.z; acc[7] += uj * k1.w;
-      }
-      __syncthreads();  // every read of the old slice (and of this chunk's data) is done
+    for (int tc = 0; tc < 2; ++tc) {
+      floatx4 acc;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sS[c][d0 + e] = acc[e];
+      for (int q = 0; q < 4; ++q) acc[q] = cgc * sS[16 * tc + 4 * lk + q][16 * wave + li];
+#pragma unroll 8
+      for (int k = 0; k < kC / 4; ++k)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[4 * k + lk][16 * tc + li], sK[4 * k + lk][16 * wave + li], acc,
+                                                   0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sS[16 * tc + 4 * lk + q][16 * wave + li] = acc[q];
     }
-    if (chunk + 1 < p.n_chunks) {
-      store_chunk(nxt);
-      cur = nxt;
-    }
-    __syncthreads();
+    __syncthreads();  // every read of this chunk's data and of the new S is done
   }
   if (p.s_final != nullptr)
     for (int i = tid; i < kSlice * kD; i += kScanThreads) {
