@@ -19,7 +19,8 @@
 //     O = diag(G) Q S0^T + A U,  A[t][j] = (G_t / G_j) q_t.k_j  (j <= t),
 //     S_end = G_C S0 + U^T diag(G_C / G) K.
 // Wt, Ut, A, diag(G) Q and diag(G_C/G) K depend on the chunk only, so one
-// kernel computes them for every (head, chunk) in parallel; a second walks
+// kernel computes them for every (key head, chunk) in parallel, sharing k.k^T
+// and q.k^T among the value heads of a key head; a second walks
 // the chunks in order per (head, 32-row slice of S): the rows of S evolve
 // independently, so slices need no communication.
 #include <hip/hip_runtime.h>
@@ -119,19 +120,23 @@ __device__ inline float wave_prefix_sum(float x, int lane) {
   return x;
 }
 
+// One workgroup per (chunk, key head): the q/k rows, k.k^T and q.k^T once,
+// then, for each value head reading that key head, its decay and write
+// strength applied and the forward substitution.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(GdnArgs p, float* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) float sk[kC][kP];  // k rows (normalized)
   __shared__ __attribute__((aligned(16))) float sq[kC][kP];  // q rows (normalized, scaled)
+  __shared__ __attribute__((aligned(16))) float sw[kC][kP];  // right-hand sides / solution, Wt half
+  __shared__ __attribute__((aligned(16))) float sv[kC][kP];  // right-hand sides / solution, Ut half
   __shared__ __attribute__((aligned(16))) float sm[kC][kPA];  // M (strictly lower)
   __shared__ float sgam[kC];     // cumulative log decay
   __shared__ float sbeta[kC];
 
-  const int chunk = blockIdx.x, h = blockIdx.y;
-  const int hk = h / (p.hv / p.hk);
+  const int chunk = blockIdx.x, hk = blockIdx.y;
+  const int rep = p.hv / p.hk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t0 = (int64_t)chunk * kC;
-  float* out = ws + ((int64_t)h * p.n_chunks + chunk) * kWsPerChunk;
 
   // q, k rows of the chunk (zero beyond T: such tokens have beta = 0, g = 0
   // and leave the state unchanged); thread -> row tid/4, quarter tid%4, all
@@ -165,93 +170,109 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(GdnArgs p, float* __
     store32(&sk[t][part * 32], kr);
     store32(&sq[t][part * 32], qr);
   }
-  if (wave == 0) {
-    const int64_t tt = t0 + lane;
-    float b = 0.0f, g = 0.0f;
-    if (tt < p.T) {
-      b = load_elem<DT>(p.beta, tt * p.ld_beta + h);
-      g = load_elem<DT>(p.g, tt * p.ld_g + h);
-    }
-    sbeta[lane] = b;
-    sgam[lane] = wave_prefix_sum(g, lane);
-  }
   __syncthreads();
 
-  // M[t][j] = beta_t exp(gam_t - gam_j) k_t.k_j (j < t) and
-  // A[t][j] = exp(gam_t - gam_j) q_t.k_j (j <= t): thread -> row t, 16 columns
-  {
-    const int t = tid >> 2, j0 = (tid & 3) * 16;
-    float km[16], qm[16];
+  // k_t.k_j and q_t.k_j: thread -> row t, 16 columns, kept in registers for
+  // every value head of the group
+  const int mt = tid >> 2, j0 = (tid & 3) * 16;
+  float km[16], qm[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) km[i] = qm[i] = 0.0f;
-    for (int d = 0; d < kD; d += 4) {
-      const float4 kt = *reinterpret_cast<const float4*>(&sk[t][d]);
-      const float4 qt = *reinterpret_cast<const float4*>(&sq[t][d]);
+  for (int i = 0; i < 16; ++i) km[i] = qm[i] = 0.0f;
+  for (int d = 0; d < kD; d += 4) {
+    const float4 kt = *reinterpret_cast<const float4*>(&sk[mt][d]);
+    const float4 qt = *reinterpret_cast<const float4*>(&sq[mt][d]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float4 kj = *reinterpret_cast<const float4*>(&sk[j0 + i][d]);
-        km[i] += kt.x * kj.x + kt.y * kj.y + kt.z * kj.z + kt.w * kj.w;
-        qm[i] += qt.x * kj.x + qt.y * kj.y + qt.z * kj.z + qt.w * kj.w;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const float4 kj = *reinterpret_cast<const float4*>(&sk[j0 + i][d]);
+      km[i] += kt.x * kj.x + kt.y * kj.y + kt.z * kj.z + kt.w * kj.w;
+      qm[i] += qt.x * kj.x + qt.y * kj.y + qt.z * kj.z + qt.w * kj.w;
     }
+  }
+
+  for (int hr = 0; hr < rep; ++hr) {
+    const int h = hk * rep + hr;
+    float* out = ws + ((int64_t)h * p.n_chunks + chunk) * kWsPerChunk;
+    if (wave == 0) {
+      const int64_t tt = t0 + lane;
+      float b = 0.0f, g = 0.0f;
+      if (tt < p.T) {
+        b = load_elem<DT>(p.beta, tt * p.ld_beta + h);
+        g = load_elem<DT>(p.g, tt * p.ld_g + h);
+      }
+      sbeta[lane] = b;
+      sgam[lane] = wave_prefix_sum(g, lane);
+    }
+    // this head's v rows, issued early
+    float vr[32];
+    {
+      const int t = tid >> 2, part = tid & 3;
+      load32<DT>(p.v, (t0 + t) * p.ld_v + (int64_t)h * kD + part * 32, t0 + t < p.T, vr);
+    }
+    __syncthreads();  // beta, gamma of this head; every read of the previous head's buffers done
+
+    // M[t][j] = beta_t exp(gam_t - gam_j) k_t.k_j (j < t) and
+    // A[t][j] = exp(gam_t - gam_j) q_t.k_j (j <= t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = j0 + i;
-      const float dec = expf(sgam[t] - sgam[j]);
-      sm[t][j] = j < t ? sbeta[t] * dec * km[i] : 0.0f;
-      out[kWsA + t * kC + j] = j <= t ? dec * qm[i] : 0.0f;
+      const float dec = expf(sgam[mt] - sgam[j]);
+      sm[mt][j] = j < mt ? sbeta[mt] * dec * km[i] : 0.0f;
+      out[kWsA + mt * kC + j] = j <= mt ? dec * qm[i] : 0.0f;
     }
-  }
-  __syncthreads();
-
-  // diag(G) Q goes out now: the q rows' LDS then holds the chunk's v rows
-  for (int i = tid; i < kC * kD; i += kThreads) out[kWsQ + i] = expf(sgam[i / kD]) * sq[i / kD][i % kD];
-  __syncthreads();
-  {
-    const int t = tid >> 2, part = tid & 3;
-    float vr[32];
-    load32<DT>(p.v, (t0 + t) * p.ld_v + (int64_t)h * kD + part * 32, t0 + t < p.T, vr);
-    store32(&sq[t][part * 32], vr);
-  }
-  __syncthreads();
-
-  // diag(G_C / G) K and G_C go out before the k rows are overwritten
-  const float gc = sgam[kC - 1];
-  for (int i = tid; i < kC * kD; i += kThreads) out[kWsK + i] = expf(gc - sgam[i / kD]) * sk[i / kD][i % kD];
-  if (tid == 0) out[kWsG] = expf(gc);
-  __syncthreads();  // every read of the k rows is done before they are overwritten
-
-  // [Wt | Ut] = (I + M)^-1 diag(beta) [diag(G) K | V] by forward substitution
-  // in place: thread c owns column c of [k rows | v rows] (a wave's columns
-  // are all of one kind); 16 rows at a time in registers, earlier rows read
-  // back final from LDS, M read as a broadcast.
-  {
-    const bool wcol = tid < kD;
-    const int cc = tid & (kD - 1);
-    float* col = wcol ? &sk[0][cc] : &sq[0][cc];  // element t at col[t * kP]
-    for (int t = 0; t < kC; ++t) col[t * kP] *= sbeta[t] * (wcol ? expf(sgam[t]) : 1.0f);
-    for (int b0 = 0; b0 < kC; b0 += 16) {
-      float r[16];
+    // diag(G) Q, diag(G_C / G) K, G_C, and the right-hand sides
+    // beta diag(G) K and beta V
+    const float gc = sgam[kC - 1];
+    {
+      const int t = tid >> 2, part = tid & 3;
+      const float eg = expf(sgam[t]), egc = expf(gc - sgam[t]), bt = sbeta[t];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) r[i] = col[(b0 + i) * kP];
-      for (int j = 0; j < b0; j += 4) {  // b0 is a multiple of 16
-        const float y0 = col[j * kP], y1 = col[(j + 1) * kP], y2 = col[(j + 2) * kP], y3 = col[(j + 3) * kP];
+      for (int e = 0; e < 32; e += 4) {
+        const int d = part * 32 + e;
+        const float4 kv = *reinterpret_cast<const float4*>(&sk[t][d]);
+        const float4 qv = *reinterpret_cast<const float4*>(&sq[t][d]);
+        *reinterpret_cast<float4*>(out + kWsQ + t * kD + d) = make_float4(eg * qv.x, eg * qv.y, eg * qv.z, eg * qv.w);
+        *reinterpret_cast<float4*>(out + kWsK + t * kD + d) =
+            make_float4(egc * kv.x, egc * kv.y, egc * kv.z, egc * kv.w);
+        const float s = bt * eg;
+        *reinterpret_cast<float4*>(&sw[t][d]) = make_float4(s * kv.x, s * kv.y, s * kv.z, s * kv.w);
+        *reinterpret_cast<float4*>(&sv[t][d]) =
+            make_float4(bt * vr[e], bt * vr[e + 1], bt * vr[e + 2], bt * vr[e + 3]);
+      }
+    }
+    if (tid == 0) out[kWsG] = expf(gc);
+    __syncthreads();
+
+    // [Wt | Ut] = (I + M)^-1 [rhs] by forward substitution in place: thread c
+    // owns column c of [sw | sv] (a wave's columns are all of one kind); 16
+    // rows at a time in registers, earlier rows read back final from LDS, M
+    // read as a broadcast
+    {
+      const bool wcol = tid < kD;
+      const int cc = tid & (kD - 1);
+      float* col = wcol ? &sw[0][cc] : &sv[0][cc];  // element t at col[t * kP]
+      for (int b0 = 0; b0 < kC; b0 += 16) {
+        float r[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) r[i] = col[(b0 + i) * kP];
+        for (int j = 0; j < b0; j += 4) {  // b0 is a multiple of 16
+          const float y0 = col[j * kP], y1 = col[(j + 1) * kP], y2 = col[(j + 2) * kP], y3 = col[(j + 3) * kP];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float4 m = *reinterpret_cast<const float4*>(&sm[b0 + i][j]);
+            r[i] -= m.x * y0 + m.y * y1 + m.z * y2 + m.w * y3;
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float4 m = *reinterpret_cast<const float4*>(&sm[b0 + i][j]);
-          r[i] -= m.x * y0 + m.y * y1 + m.z * y2 + m.w * y3;
+#pragma unroll
+          for (int jj = 0; jj < i; ++jj) r[i] -= sm[b0 + i][b0 + jj] * r[jj];
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) col[(b0 + i) * kP] = r[i];
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int jj = 0; jj < i; ++jj) r[i] -= sm[b0 + i][b0 + jj] * r[jj];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) col[(b0 + i) * kP] = r[i];
+      float* dst = out + (wcol ? kWsW : kWsU);
+      for (int t = 0; t < kC; ++t) dst[t * kD + cc] = col[t * kP];
     }
-    float* dst = out + (wcol ? kWsW : kWsU);
-    for (int t = 0; t < kC; ++t) dst[t * kD + cc] = col[t * kP];
   }
 }
 
@@ -405,7 +426,7 @@ size_t gdn_workspace_floats(int64_t T, int hv) {
 }
 
 hipError_t launch_gdn(const GdnArgs& p, float* ws, hipStream_t s) {
-  const dim3 prep((unsigned)p.n_chunks, (unsigned)p.hv);
+  const dim3 prep((unsigned)p.n_chunks, (unsigned)p.hk);
   if (p.in_dtype == NVFP4_DTYPE_BF16)
     gdn_prep_kernel<NVFP4_DTYPE_BF16><<<prep, kThreads, 0, s>>>(p, ws);
   else
