@@ -39,29 +39,31 @@ __device__ inline float block_max(float v) {
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Load one 16-element block starting at p (16-byte aligned) as floats.
+// One 16-element block as raw words: 2 x 16 bytes (bf16) or 4 x 16 bytes (f32).
 template <int DT>
-__device__ inline void load_block16(const uint8_t* p, float v[16]) {
-  if constexpr (DT == NVFP4_DTYPE_BF16) {
-    const uint4 q0 = *reinterpret_cast<const uint4*>(p);
-    const uint4 q1 = *reinterpret_cast<const uint4*>(p + 16);
-    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+struct RawBlock {
+  static constexpr int kVec = DT == NVFP4_DTYPE_BF16 ? 2 : 4;
+  uint4 q[kVec];
+  __device__ void load(const uint8_t* p) {  // p 16-byte aligned
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
+    for (int i = 0; i < kVec; ++i) q[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
+  }
+  __device__ void to_float(float v[16]) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 q = *reinterpret_cast<const float4*>(p + 16 * i);
-      v[4 * i] = q.x;
-      v[4 * i + 1] = q.y;
-      v[4 * i + 2] = q.z;
-      v[4 * i + 3] = q.w;
+    for (int i = 0; i < kVec; ++i) {
+      const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (DT == NVFP4_DTYPE_BF16) {
+          v[8 * i + 2 * j] = bf16_lo(w[j]);
+          v[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+        } else {
+          v[4 * i + j] = __uint_as_float(w[j]);
+        }
+      }
     }
   }
-}
+};
 
 // Walks the 16-element blocks of a [rows, bpr*16] matrix with a grid-stride
 // loop, keeping (row, block-in-row) without a division per step.
@@ -95,8 +97,10 @@ __global__ __launch_bounds__(kElemThreads) void amax_kernel(const uint8_t* __res
   constexpr int kBlockBytes = DT == NVFP4_DTYPE_BF16 ? 32 : 64;
   float m = 0.0f;
   for (BlockWalk it(rows, bpr); it.valid(); it.next()) {
+    RawBlock<DT> b;
+    b.load(x + it.r * ld_bytes + it.j * kBlockBytes);
     float v[16];
-    load_block16<DT>(x + it.r * ld_bytes + it.j * kBlockBytes, v);
+    b.to_float(v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
   }
@@ -121,13 +125,29 @@ __global__ __launch_bounds__(kElemThreads) void quantize_kernel(
   } else {
     g = *gptr;
   }
-  for (BlockWalk it(rows, bpr); it.valid(); it.next()) {
+  // Software-pipelined: the next block's load is issued before this block's
+  // stores, so waiting for a load never waits for earlier stores (loads and
+  // stores share one counter).  Past the end the load re-reads the current
+  // block (a valid address) rather than branching around it.
+  BlockWalk it(rows, bpr);
+  if (!it.valid()) return;
+  RawBlock<DT> cur;
+  cur.load(x + it.r * ld_bytes + it.j * kBlockBytes);
+  while (true) {
+    BlockWalk nx = it;
+    nx.next();
+    const bool more = nx.valid();
+    RawBlock<DT> nb;
+    nb.load(x + (more ? nx.r : it.r) * ld_bytes + (more ? nx.j : it.j) * kBlockBytes);
     float v[16];
-    load_block16<DT>(x + it.r * ld_bytes + it.j * kBlockBytes, v);
+    cur.to_float(v);
     uint2 c;
     const uint32_t s = dev::quantize_block16(v, g, &c);
     *reinterpret_cast<uint2*>(codes + it.r * ld_codes + it.j * 8) = c;
     scales[it.r * ld_scales + it.j] = (uint8_t)s;
+    if (!more) break;
+    cur = nb;
+    it = nx;
   }
 }
 

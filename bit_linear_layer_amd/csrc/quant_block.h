@@ -1,5 +1,8 @@
 // Exact NVFP4 quantization of one 16-element block, shared by the quantize
-// pass and the GEMM epilogue that quantizes its own output.
+// pass and the GEMM epilogue that quantizes its own output.  Blocks take a
+// bracketed path on the hardware E2M1 pack with an exact per-element repair
+// (quantize_block16); scales outside float32's comfortable range take the
+// threshold count below.
 //
 // Format (evolve.pub review of arXiv 2609.04098, "Scope & Claims";
 // thevalue.engineering article, section on the fragility myth): E2M1 codes
@@ -10,9 +13,10 @@
 // s, the magnitude code of x is the number of E2M1 midpoints mu in {0.25,
 // 0.75, 1.25, 1.75, 2.5, 3.5, 5} that |x| passes, where "passes" is > for
 // the midpoints whose tie goes down (to an even code) and >= for those whose
-// tie goes up.  |x| has <= 24 significant bits, mu * s * g <= 3 + 4 + 24 = 31
-// bits, so both are exact float64 numbers and the float64 comparisons are the
-// exact-real decisions.  The block scale is one correctly rounded float64
+// tie goes up.  mu * s * g <= 3 + 4 + 24 = 31 bits is an exact float64
+// number; |x| is a float32, so "|x| > t" is "|x| >= the next float32 above
+// t" and "|x| >= t" is "|x| >= the smallest float32 not below t" -- one exact
+// float32 bound per threshold and block.  The block scale is one correctly rounded float64
 // division amax_b / (6 g): a non-tie quotient lies >= 2^-31 (relative) from
 // every E4M3 midpoint, far above float64's 2^-53 rounding, so rounding the
 // float64 quotient to E4M3 is exact.
@@ -40,33 +44,118 @@ __device__ inline double e4m3_value(uint32_t code) {
   return e == 0 ? (double)m * 0x1p-9 : ldexp(1.0 + (double)m * 0.125, (int)e - 7);
 }
 
+// Smallest float32 c with c >= t (strict: c > t), for a float64 t >= 0:
+// for a float32 x, x >= t <=> x >= c (strict: x > t <=> x >= c).  Values
+// beyond the float32 range give +inf (no float32 passes them).
+__device__ inline float f32_ceil_bound(double t, bool strict) {
+  float c = (float)t;  // nearest; may lie below t
+  if ((double)c < t || (strict && (double)c == t)) c = __uint_as_float(__float_as_uint(c) + 1u);
+  return c;
+}
+
+// Exact magnitude-count rounding of v[0..15] under block scale code s and
+// global scale g.  The seven thresholds mu * s * g are exact float64
+// numbers; each becomes a float32 bound once per block (f32_ceil_bound, with
+// > or >= per midpoint's tie direction), so every element takes its exact
+// decisions with float32 comparisons.
+__device__ inline uint2 codes_by_thresholds(const float v[16], uint32_t s, float g) {
+  float b0, b1, b2, b3, b4, b5, b6;
+  if (s == 0) {  // every magnitude code is 0
+    b0 = b1 = b2 = b3 = b4 = b5 = b6 = __builtin_inff();
+  } else {
+    const double sg = e4m3_value(s) * (double)g;
+    b0 = f32_ceil_bound(0.25 * sg, true);  b1 = f32_ceil_bound(0.75 * sg, false);
+    b2 = f32_ceil_bound(1.25 * sg, true);  b3 = f32_ceil_bound(1.75 * sg, false);
+    b4 = f32_ceil_bound(2.5 * sg, true);   b5 = f32_ceil_bound(3.5 * sg, false);
+    b6 = f32_ceil_bound(5.0 * sg, true);
+  }
+  uint32_t word[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = fabsf(v[i]);
+    uint32_t c = (a >= b0) + (a >= b1) + (a >= b2) + (a >= b3) + (a >= b4) + (a >= b5) + (a >= b6);
+    c |= (__float_as_uint(v[i]) >> 31) << 3;
+    word[i >> 3] |= c << (4 * (i & 7));
+  }
+  return make_uint2(word[0], word[1]);
+}
+
+// E4M3 (OCP FN) magnitude code -> float32, exact (no NaN code reaches here).
+__device__ inline float e4m3_value_f32(uint32_t code) {
+  return code < 8u ? (float)code * 0x1p-9f : __uint_as_float((code + (120u << 3)) << 20);
+}
+
+// Byte P of lo / hi <- E2M1 codes of (a, b) times r_lo / r_hi (a in the low nibble).
+template <int P>
+__device__ inline void pack_pair(uint32_t& lo, uint32_t& hi, float a, float b, float r_lo, float r_hi) {
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, a * r_lo, b * r_lo, 1.0f, P);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, a * r_hi, b * r_hi, 1.0f, P);
+}
+
 // Quantize v[0..15] with global scale g: 8 code bytes (low nibble = even
 // element) in *codes, the E4M3 scale byte returned.
+//
+// Bracketed fast path.  With S = fl32(s * g) in [2^-90, 2^126] and
+// R = rcp(S) (within 2^-23 of 1/S), R_lo = R (1 - 2^-18) and
+// R_hi = R (1 + 2^-18) put fl32(x R_lo) and fl32(x R_hi) on either side of
+// the exact quotient x / (s g): the margin 2^-18 exceeds the sum of the four
+// roundings (2^-24 each) and rcp's 2^-23.  gfx950's E2M1 pack instruction
+// rounds to the nearest code with ties to even, saturates beyond 6 and keeps
+// the sign of zero -- the same map as the exact definition -- and that map is
+// monotone, so where both products give the same code, so does the exact
+// quotient.  Products that underflow lie far below the first midpoint.
+//
+// Where the two codes differ (magnitudes m and m + 1: the bracket is far
+// narrower than the gap between midpoints), the exact quotient sits next to
+// the midpoint mu_m, and one fused multiply-add decides: mu_m * s is exact in
+// float32 (<= 9 bits), fma(mu_m s, g, -|x|) rounds the exact difference once,
+// so its sign is exact (zero only on a tie, which goes to the even code; with
+// S >= 2^-90 a nonzero difference is a normal float32).  Bf16 data hits this
+// often: with g = amax / 2688, many quotients fall within 2^-24 of a
+// midpoint.  s == 0 gives R = 0: every product is a signed zero, the exact
+// answer.  S outside the range above takes the threshold count.
 __device__ inline uint32_t quantize_block16(const float v[16], float g, uint2* codes) {
-  const double g64 = (double)g;
   float amax_b = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
 
   uint32_t s = 0;
-  if (g != 0.0f && amax_b != 0.0f) s = e4m3_rne((double)amax_b / (6.0 * g64));  // 6 g is exact
+  if (g != 0.0f && amax_b != 0.0f) s = e4m3_rne((double)amax_b / (6.0 * (double)g));  // 6 g is exact
 
-  // thresholds mu * s * g, exact in float64; s == 0 -> every magnitude code is 0
-  double t0, t1, t2, t3, t4, t5, t6;
-  if (s == 0) {
-    t0 = t1 = t2 = t3 = t4 = t5 = t6 = __builtin_inf();
-  } else {
-    const double sg = e4m3_value(s) * g64;
-    t0 = 0.25 * sg; t1 = 0.75 * sg; t2 = 1.25 * sg; t3 = 1.75 * sg;
-    t4 = 2.5 * sg;  t5 = 3.5 * sg;  t6 = 5.0 * sg;
+  const float sv = e4m3_value_f32(s);
+  const float S = sv * g;
+  if (s != 0u && !(S >= 0x1p-90f && S <= 0x1p126f)) {
+    *codes = codes_by_thresholds(v, s, g);
+    return s;
   }
-  uint32_t word[2] = {0u, 0u};
+  const float R = s == 0u ? 0.0f : __builtin_amdgcn_rcpf(S);
+  const float r_lo = R * (1.0f - 0x1p-18f), r_hi = R * (1.0f + 0x1p-18f);
+  uint32_t lo0 = 0u, lo1 = 0u, hi0 = 0u, hi1 = 0u;
+  pack_pair<0>(lo0, hi0, v[0], v[1], r_lo, r_hi);    pack_pair<0>(lo1, hi1, v[8], v[9], r_lo, r_hi);
+  pack_pair<1>(lo0, hi0, v[2], v[3], r_lo, r_hi);    pack_pair<1>(lo1, hi1, v[10], v[11], r_lo, r_hi);
+  pack_pair<2>(lo0, hi0, v[4], v[5], r_lo, r_hi);    pack_pair<2>(lo1, hi1, v[12], v[13], r_lo, r_hi);
+  pack_pair<3>(lo0, hi0, v[6], v[7], r_lo, r_hi);    pack_pair<3>(lo1, hi1, v[14], v[15], r_lo, r_hi);
+
+  const float mu_scale = 0.25f * sv;  // mu_m * s = (4 mu_m) * mu_scale, exact
+  uint32_t word[2] = {lo0, lo1};
+  const uint32_t hi[2] = {hi0, hi1};
+  const uint32_t diff[2] = {lo0 ^ hi0, lo1 ^ hi1};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const double a = (double)fabsf(v[i]);
-    uint32_t c = (a > t0) + (a >= t1) + (a > t2) + (a >= t3) + (a > t4) + (a >= t5) + (a > t6);
-    c |= (__float_as_uint(v[i]) >> 31) << 3;
-    word[i >> 3] |= c << (4 * (i & 7));
+  for (int q = 0; q < 4; ++q) {  // groups of 4 elements: most waves skip most groups
+    const int w = q >> 1;
+    if ((diff[w] >> (16 * (q & 1))) & 0xFFFFu) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * q + e, sh = 4 * (i & 7);
+        if ((diff[w] >> sh) & 0xFu) {
+          const uint32_t m = (word[w] >> sh) & 7u;
+          const uint32_t mu4 = m < 4u ? 2u * m + 1u : (m == 6u ? 20u : 4u * m - 6u);  // 4 x {.25 .75 1.25 1.75 2.5 3.5 5}
+          const float d = fmaf((float)mu4 * mu_scale, g, -fabsf(v[i]));
+          const bool up = d < 0.0f || (d == 0.0f && (m & 1u));
+          if (up) word[w] = (word[w] & ~(0xFu << sh)) | (hi[w] & (0xFu << sh));
+        }
+      }
+    }
   }
   *codes = make_uint2(word[0], word[1]);
   return s;
