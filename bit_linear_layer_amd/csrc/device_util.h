@@ -103,6 +103,16 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
 
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two floats -> packed bf16 (a in the low half) with gfx950's conversion
+// instruction: round to nearest even, the same as f32_to_bf16_bits for every
+// finite input (checked on the device, ties and subnormals included).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
 // silu(u) = u * sigmoid(u), with sigmoid evaluated without overflow.  The
 // SiLU*mul kernel and the fused gate_up epilogue both call this one
 // definition, so their bf16 results agree bit for bit.

@@ -6,16 +6,24 @@
 // fl32(e4m3 * s), optionally rounded to bf16.  s = 1 is the uncalibrated
 // cache, so calibrated and uncalibrated caches run the same code.
 //
-// Exactness of the write without a division per element: the float32
-// estimate r = |x| * fl32(1/s) is within 2 ulps of the exact quotient, so
-// truncating it to the E4M3 grid names the code `lo` just below the quotient
-// and the midpoint above it (away from a grid point by far more than 2 ulps).
-// The midpoint has <= 5 significant bits and is exact in float32, s has 24,
-// so midpoint * s is an exact float64 number and comparing |x| with it (a
-// tie goes to the even code) is the exact-real decision.  No lane branches,
-// so calibrated and unit scales cost the same.  Subnormal scales, whose
-// reciprocal overflows, divide in float64 instead (e4m3_rne, exact by the
-// same bit counts).
+// The write without a division per element.  With R = 1/s and the bracket
+// R_lo = R (1 - 2^-18), R_hi = R (1 + 2^-18), the float32 products x R_lo and
+// x R_hi lie on either side of the exact quotient x / s (the margin exceeds
+// the roundings of R and of the products); clamped to +-448, both go through
+// gfx950's E4M3 conversion, which rounds to nearest with ties to even (and
+// keeps the sign of zero) but does not saturate -- hence the clamp, which is
+// the saturating rule's own answer.  Where both bytes agree that byte is
+// exact (the map is monotone).  Where they differ (codes m and m + 1, the
+// bracket being far narrower than a grid step) the quotient sits next to the
+// midpoint mu between the two values; mu has <= 5 significant bits, so
+// fma(mu, s, -|x|) rounds the exact difference once and its sign decides
+// (zero on a tie, which goes to the even code).  Scales outside [2^-90,
+// 2^126] -- where that difference could leave float32's normal range --
+// divide in float64 instead (e4m3_rne, exact by the bit counts).  A power-of-
+// two scale (the unit scale among them) needs no bracket: x / s is then an
+// exact float32 product and one conversion is the answer.  The read
+// decodes with the hardware conversion (exact for every byte) and rounds to
+// bf16 with the hardware conversion (nearest even).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,31 +78,58 @@ struct ChunkWalk {
   }
 };
 
-// E4M3 (OCP FN) byte -> float, exact.  Normal: the 7 magnitude bits are the
-// float32 exponent/mantissa fields shifted, exponent rebased 7 -> 127
-// (+120 << 3); subnormal: m * 2^-9.
-__device__ inline float e4m3_to_f32(uint32_t b) {
-  const uint32_t mag = b & 0x7Fu;
-  const float v = mag < 8u ? (float)mag * 0x1p-9f : __uint_as_float((mag + 960u) << 20);
-  return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
+// Magnitude of the E4M3 byte P of `src`, decoded by the hardware conversion (exact).
+template <int P>
+__device__ inline float e4m3_byte_mag(uint32_t src) {
+  return fabsf(__builtin_amdgcn_cvt_f32_fp8((int)src, P));
 }
 
-// Magnitude code (0..0x7E) of the E4M3 value nearest to the exact real
-// ax / s (ax >= 0), ties to the even code, saturating at 448.  Branch-free:
-// r names the code `lo` just below the quotient and the midpoint above it;
-// one exact float64 comparison decides.
-__device__ inline uint32_t e4m3_quotient_code(float ax, float inv_s, double s) {
-  const float r = ax * inv_s;
-  const uint32_t b = __float_as_uint(r);
-  const float t = r * 512.0f;  // subnormal grid k * 2^-9 (k = 8 is the smallest normal)
-  const float k = floorf(t);
-  const bool normal = r >= 0x1p-6f;
-  const uint32_t lo = normal ? (b >> 20) - (120u << 3) : (uint32_t)k;  // mantissa truncated to 3 bits
-  const float mid = normal ? __uint_as_float((b & 0xFFF00000u) | 0x80000u) : (k + 0.5f) * 0x1p-9f;
-  const double m = (double)mid * s;  // exact: <= 5 bits times 24 bits
-  const double a = (double)ax;
-  const uint32_t up = (a > m || (a == m && (lo & 1u))) ? 1u : 0u;  // a tie goes to the even code
-  return min(lo + up, 0x7Eu);
+// Bracket repair of byte P: lo and hi differ there (magnitudes m, m + 1).
+template <int P>
+__device__ inline void repair_byte(uint32_t& word, uint32_t lo, uint32_t hi, float x, float s) {
+  constexpr int sh = 8 * P;
+  if (((lo ^ hi) >> sh) & 0xFFu) {
+    const float mid = 0.5f * (e4m3_byte_mag<P>(lo) + e4m3_byte_mag<P>(hi));  // exact, <= 5 bits
+    const float d = fmaf(mid, s, -fabsf(x));
+    const bool up = d < 0.0f || (d == 0.0f && ((lo >> sh) & 1u));
+    if (up) word = (word & ~(0xFFu << sh)) | (hi & (0xFFu << sh));
+  }
+}
+
+// Four E4M3 bytes (element 0 in the low byte) of x[0..3] * r with r = 1/s a
+// power of two: the products are exact (or far below the first midpoint, or
+// clamped), so one conversion is the exact answer.
+__device__ inline uint32_t e4m3_quad_exact(const float* x, float r) {
+  const float y0 = __builtin_amdgcn_fmed3f(x[0] * r, -448.0f, 448.0f);
+  const float y1 = __builtin_amdgcn_fmed3f(x[1] * r, -448.0f, 448.0f);
+  const float y2 = __builtin_amdgcn_fmed3f(x[2] * r, -448.0f, 448.0f);
+  const float y3 = __builtin_amdgcn_fmed3f(x[3] * r, -448.0f, 448.0f);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)w, true);
+}
+
+// Four E4M3 bytes (element 0 in the low byte) of x[0..3] / s, exactly rounded.
+__device__ inline uint32_t e4m3_quad(const float* x, float r_lo, float r_hi, float s) {
+  const float l0 = __builtin_amdgcn_fmed3f(x[0] * r_lo, -448.0f, 448.0f);
+  const float l1 = __builtin_amdgcn_fmed3f(x[1] * r_lo, -448.0f, 448.0f);
+  const float l2 = __builtin_amdgcn_fmed3f(x[2] * r_lo, -448.0f, 448.0f);
+  const float l3 = __builtin_amdgcn_fmed3f(x[3] * r_lo, -448.0f, 448.0f);
+  const float h0 = __builtin_amdgcn_fmed3f(x[0] * r_hi, -448.0f, 448.0f);
+  const float h1 = __builtin_amdgcn_fmed3f(x[1] * r_hi, -448.0f, 448.0f);
+  const float h2 = __builtin_amdgcn_fmed3f(x[2] * r_hi, -448.0f, 448.0f);
+  const float h3 = __builtin_amdgcn_fmed3f(x[3] * r_hi, -448.0f, 448.0f);
+  uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
+  lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l2, l3, (int)lo, true);
+  uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h0, h1, 0, false);
+  hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h2, h3, (int)hi, true);
+  uint32_t word = lo;
+  if (lo != hi) {
+    repair_byte<0>(word, lo, hi, x[0], s);
+    repair_byte<1>(word, lo, hi, x[1], s);
+    repair_byte<2>(word, lo, hi, x[2], s);
+    repair_byte<3>(word, lo, hi, x[3], s);
+  }
+  return word;
 }
 
 template <int DT>
@@ -104,20 +139,29 @@ __global__ __launch_bounds__(kElemThreads) void kv_quant_kernel(
     int64_t ld_cache, const float* __restrict__ scale) {
   constexpr int kChunkBytes = DT == NVFP4_DTYPE_BF16 ? 16 : 32;
   const float sf = *scale;
-  const float inv_s = 1.0f / sf;
+  const bool fast = sf >= 0x1p-90f && sf <= 0x1p126f;  // uniform over the launch
+  const bool pow2 = fast && (__float_as_uint(sf) & 0x7FFFFFu) == 0u;  // 1/s exact (s = 1 among them)
+  const float R = 1.0f / sf;
+  const float r_lo = R * (1.0f - 0x1p-18f), r_hi = R * (1.0f + 0x1p-18f);
   const double s = (double)sf;
-  const bool fast = inv_s < 0x1p127f;  // 1/s overflows only for subnormal s: divide instead
   for (ChunkWalk it(rows, cpr); it.valid(); it.next()) {
     const int64_t dst = slots != nullptr ? slots[it.r] : it.r;
     if (dst < 0 || dst >= cache_rows) continue;  // documented: such rows are not written
     float v[8];
     load8<DT>(x + it.r * ld_bytes + it.c * kChunkBytes, v);
     uint32_t w[2] = {0u, 0u};
+    if (pow2) {
+      w[0] = e4m3_quad_exact(v, R);
+      w[1] = e4m3_quad_exact(v + 4, R);
+    } else if (fast) {
+      w[0] = e4m3_quad(v, r_lo, r_hi, sf);
+      w[1] = e4m3_quad(v + 4, r_lo, r_hi, sf);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t m = fast ? e4m3_quotient_code(fabsf(v[e]), inv_s, s) : e4m3_rne((double)fabsf(v[e]) / s);
-      const uint32_t b = m | ((__float_as_uint(v[e]) >> 31) << 7);
-      w[e >> 2] |= b << (8 * (e & 3));
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t m = e4m3_rne((double)fabsf(v[e]) / s);
+        w[e >> 2] |= (m | ((__float_as_uint(v[e]) >> 31) << 7)) << (8 * (e & 3));
+      }
     }
     *reinterpret_cast<uint2*>(cache + dst * ld_cache + it.c * 8) = make_uint2(w[0], w[1]);
   }
@@ -130,14 +174,15 @@ __global__ __launch_bounds__(kElemThreads) void kv_dequant_kernel(
   const float s = *scale;
   for (ChunkWalk it(rows, cpr); it.valid(); it.next()) {
     const uint2 q = *reinterpret_cast<const uint2*>(cache + it.r * ld_cache + it.c * 8);
-    const uint32_t w[2] = {q.x, q.y};
     float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = e4m3_to_f32((w[e >> 2] >> (8 * (e & 3))) & 0xFFu) * s;
+    const f32x2_t d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false), d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
+    const f32x2_t d2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false), d3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
+    f[0] = d0.x * s; f[1] = d0.y * s; f[2] = d1.x * s; f[3] = d1.y * s;
+    f[4] = d2.x * s; f[5] = d2.y * s; f[6] = d3.x * s; f[7] = d3.y * s;
     if constexpr (OUT == NVFP4_DTYPE_BF16) {
       uint32_t h[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+      for (int i = 0; i < 4; ++i) h[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
       *reinterpret_cast<uint4*>(out + it.r * ld_out_bytes + it.c * 16) = make_uint4(h[0], h[1], h[2], h[3]);
     } else {
       float4* o = reinterpret_cast<float4*>(out + it.r * ld_out_bytes + it.c * 32);

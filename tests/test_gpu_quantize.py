@@ -6,6 +6,7 @@ import torch
 
 import bit_linear_layer_amd as nv
 import workloads as W
+from oracle import nvfp4_oracle as O
 from tests.gpu_util import DEV, assert_quant_exact, host_q, quantize_dev, say
 from tests.test_oracle_quantize import f32_from_hex, f32_hex, load_golden, tie_heavy_block
 
@@ -44,6 +45,28 @@ def test_tie_heavy_dynamic_and_static(seed):
     assert_quant_exact(xt, quantize_dev(xt))
     for g in (1.0, 2.0 ** -5, 0.37, 3e-3):
         assert_quant_exact(xt, quantize_dev(xt, g), g=np.float32(g))
+
+
+@pytest.mark.parametrize("g", [0.37109375 * 2.0 ** -8, 0.8125 * 2.0 ** -3, 3e-3])
+def test_exact_and_near_midpoints_non_power_of_two_scale(g):
+    """Blocks whose scale is pinned by an element 6 * s * g; the others sit
+    exactly on E2M1 midpoints mu * s * g (float32-exact when g has few
+    mantissa bits) or one float32 step either side of one.  Exercises the
+    kernel's exact repair of near-midpoint elements, ties included."""
+    say(f"quantize midpoints g={g}")
+    rng = np.random.default_rng(77)
+    g = np.float32(g)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    sv = O.E4M3_VALUES[rng.integers(0x20, 0x7F, size=(48, 4))]
+    x = np.empty((48, 64), np.float32)
+    for r in range(48):
+        for b in range(4):
+            t = (rng.choice(mids, 16) * sv[r, b] * float(g)).astype(np.float32)
+            t = np.where(rng.random(16) < 0.5, t, np.nextafter(t, np.float32(np.inf) * rng.choice([-1, 1], 16)))
+            t[rng.integers(16)] = np.float32(6.0 * sv[r, b] * float(g))
+            x[r, 16 * b:16 * b + 16] = t * rng.choice([-1.0, 1.0], 16).astype(np.float32)
+    xt = torch.from_numpy(x).to(DEV)
+    assert_quant_exact(xt, quantize_dev(xt, float(g)), g=g)
 
 
 def test_static_scale_saturation():
