@@ -95,10 +95,11 @@ __device__ inline void tile_of(int bid, int nblocks, int tiles_m, int tiles_n, i
   tn = in / gm;
 }
 
-// float -> bf16 bits, round to nearest even (finite inputs).
+// float -> bf16 bits, round to nearest even, with gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32; checked on the device against the integer
+// rounding (u + 0x7FFF + lsb) >> 16, ties and subnormals included).
 __device__ inline uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ inline float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
@@ -115,11 +116,17 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 
 // silu(u) = u * sigmoid(u), with sigmoid evaluated without overflow.  The
 // SiLU*mul kernel and the fused gate_up epilogue both call this one
-// definition, so their bf16 results agree bit for bit.
+// definition, so their bf16 results agree bit for bit.  e = exp(-|u|) comes
+// from the hardware exp2 (v_exp_f32) and 1 / (1 + e) from the hardware
+// reciprocal: a few float32 ulps, negligible against the bf16 rounding of
+// the result.  Below 2^-126 the exp2 argument is lifted by 64 and the result
+// scaled back by 2^-64, one rounding into the subnormal range.
 __device__ inline float silu(float u) {
-  const float e = expf(-fabsf(u));
-  const float sig = u >= 0.0f ? 1.0f / (1.0f + e) : e / (1.0f + e);
-  return u * sig;
+  const float t = -fabsf(u) * 1.44269504088896341f;  // log2(e)
+  const bool tiny = t < -126.0f;
+  const float e = __builtin_amdgcn_exp2f(tiny ? t + 64.0f : t) * (tiny ? 0x1p-64f : 1.0f);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  return u * (u >= 0.0f ? r : e * r);
 }
 
 __device__ inline float wave_max(float v) {
