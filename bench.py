@@ -31,7 +31,10 @@ METRIC = "NVFP4 W4A4 GEMM TFLOP/s incl. act-quant (M=8192) + % peak; GB/s at M=8
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_m8192_traffic.json")
-GEMM_SRC = os.path.join(ROOT, "bit_linear_layer_amd", "csrc", "gemm.hip")
+# sources the gate|up GEMM kernel is compiled from: the committed HBM
+# counters are reported only while all of them are unchanged
+GEMM_SRC = [os.path.join(ROOT, "bit_linear_layer_amd", "csrc", f)
+            for f in ("gemm.hip", "device_util.h", "quant_block.h", "internal.h")]
 
 
 def parse_args():
@@ -47,9 +50,12 @@ def parse_args():
     return ap.parse_args()
 
 
-def sha256(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sha256(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic():
