@@ -163,7 +163,11 @@ void skinny_kernel(const GemmArgs p, int n_lo, int n_hi, int groups_per_block) {
 #pragma unroll
     for (int j = 0; j < kRound; ++j) {
       if (j < ng) {
-        wait_vmem<2 * L::kDma>();  // group j landed; j+1, j+2 still fly
+        // group j landed: j+1 and j+2 still fly while they exist (the three
+        // copies before the loop are unconditional, clamped into the range)
+        if (j + 2 < ng) wait_vmem<2 * L::kDma>();
+        else if (j + 1 < ng) wait_vmem<L::kDma>();
+        else wait_vmem<0>();
         const uint8_t* st = mine + (j % kStages) * L::kStage;
         u32x4 c[QPW];
         uint32_t sc[QPW];
@@ -173,7 +177,7 @@ void skinny_kernel(const GemmArgs p, int n_lo, int n_hi, int groups_per_block) {
           sc[qi] = *reinterpret_cast<const uint16_t*>(st + L::kCodeBytes + r16 * 8 * QPW + 2 * (h * QPW + qi));
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage is in registers
-        issue(r0 + j + 3, j % kStages);       // three groups ahead
+        if (j + 3 < ng) issue(r0 + j + 3, j % kStages);  // three groups ahead, none past the round
         floatx4 a4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int qi = 0; qi < QPW; ++qi) {
@@ -187,8 +191,7 @@ void skinny_kernel(const GemmArgs p, int n_lo, int n_hi, int groups_per_block) {
         acc[j] = a4;
       }
     }
-    wait_vmem<0>();  // drain the copies issued past the round's end
-    __syncthreads();
+    __syncthreads();  // every wave has drained its copies (the last wait was vmcnt(0))
     floatx4* red = reinterpret_cast<floatx4*>(smem);  // [kRound][8 waves][64 lanes]
 #pragma unroll
     for (int j = 0; j < kRound; ++j)
