@@ -39,7 +39,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;   // head dimension (keys and values)
 constexpr int kC = 64;    // tokens per chunk
 constexpr int kSlice = 32;  // state rows per scan workgroup
-constexpr int kThreads = 256;       // prep workgroup
 constexpr int kScanThreads = 512;   // scan workgroup
 // LDS row strides, padded so the 16 rows a wave reads at once fall into
 // distinct banks (an unpadded 512-byte stride puts them all in one)
@@ -64,52 +63,6 @@ __device__ inline float load_elem(const void* base, int64_t idx) {
   }
 }
 
-// 32 consecutive elements (a quarter of a 128-wide head row) as floats, with
-// 16-byte loads (rows are 16-byte aligned); zeros when !valid.
-template <int DT>
-__device__ inline void load32(const void* base, int64_t elem, bool valid, float v[32]) {
-  if constexpr (DT == NVFP4_DTYPE_BF16) {
-    uint4 w[4];
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-    if (valid) {  // rows past the end are never read
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = src[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t x[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * j + 2 * e] = __uint_as_float(x[e] << 16);
-        v[8 * j + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
-    float4 f[8];
-    if (valid) {  // rows past the end are never read
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = src[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[4 * j] = f[j].x; v[4 * j + 1] = f[j].y; v[4 * j + 2] = f[j].z; v[4 * j + 3] = f[j].w;
-    }
-  }
-}
-
-__device__ inline void store32(float* dst, const float v[32]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    reinterpret_cast<float4*>(dst)[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-}
-
 // Inclusive prefix sum over the 64 lanes of one wave.
 __device__ inline float wave_prefix_sum(float x, int lane) {
 #pragma unroll
@@ -120,158 +73,240 @@ __device__ inline float wave_prefix_sum(float x, int lane) {
   return x;
 }
 
-// One workgroup per (chunk, key head): the q/k rows, k.k^T and q.k^T once,
-// then, for each value head reading that key head, its decay and write
-// strength applied and the forward substitution.
+// 16 consecutive elements of a head row as floats, unconditionally (the
+// caller clamps the row into range): two 16-byte loads (bf16) or four (f32).
 template <int DT>
-__global__ __launch_bounds__(kThreads) void gdn_prep_kernel(GdnArgs p, float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) float sk[kC][kP];  // k rows (normalized)
-  __shared__ __attribute__((aligned(16))) float sq[kC][kP];  // q rows (normalized, scaled)
-  __shared__ __attribute__((aligned(16))) float sw[kC][kP];  // right-hand sides / solution, Wt half
-  __shared__ __attribute__((aligned(16))) float sv[kC][kP];  // right-hand sides / solution, Ut half
+__device__ inline void load16(const void* base, int64_t elem, float v[16]) {
+  if constexpr (DT == NVFP4_DTYPE_BF16) {
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    const uint4 w0 = src[0], w1 = src[1];
+    const uint32_t x[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[2 * e] = __uint_as_float(x[e] << 16);
+      v[2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+    }
+  } else {
+    const floatx4* src = reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const floatx4 f = src[j];
+      v[4 * j] = f[0]; v[4 * j + 1] = f[1]; v[4 * j + 2] = f[2]; v[4 * j + 3] = f[3];
+    }
+  }
+}
+
+constexpr int kPrepThreads = 512;  // 8 waves
+
+// One workgroup per (chunk, key head).  Everything but the 16x16 diagonal
+// blocks of the triangular inverse runs on v_mfma_f32_16x16x4f32.  Inside a
+// product's 16-wide K block the lane group g = lane/16 takes k = 4g + s at
+// MFMA step s (any order of k gives the same sum), so an A operand is one
+// 16-byte LDS read per 4 steps and a product's accumulator (lane holds
+// D[4g + r][lane%16]) is directly the B operand of the next product.
+//   1. q, k rows, L2-normalized, into LDS; K K^T and Q K^T (waves 0-3 and
+//      4-7, one 16-row block each) stay in registers for every value head.
+//   2. per value head: M = (beta_t G_t/G_j k_t.k_j)_{j<t} into LDS, A out;
+//      T = (I + M)^-1 block by block -- diagonal 16x16 blocks by forward
+//      substitution, then T_ij = -T_ii sum_{i>k>=j} M_ik T_kj one block
+//      diagonal at a time; Wt = T diag(beta G) K and Ut = T diag(beta) V as
+//      block-triangular products.
+// The next head's v, beta, g are loaded before this head's stores, so
+// waiting for them never waits for the stores (one counter covers both).
+template <int DT>
+__global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float sk[kC][kP];   // k rows (normalized)
+  __shared__ __attribute__((aligned(16))) float sq[kC][kP];   // q rows (normalized, scaled)
+  __shared__ __attribute__((aligned(16))) float sv[kC][kP];   // v rows of the current head
   __shared__ __attribute__((aligned(16))) float sm[kC][kPA];  // M (strictly lower)
-  __shared__ float sgam[kC];     // cumulative log decay
-  __shared__ float sbeta[kC];
+  __shared__ __attribute__((aligned(16))) float st[kC][kPA];  // T = (I + M)^-1 (lower blocks)
+  __shared__ __attribute__((aligned(16))) float sgam[kC];     // cumulative log decay
+  __shared__ __attribute__((aligned(16))) float sbeta[kC];    // beta_j
+  __shared__ __attribute__((aligned(16))) float scw[kC];      // beta_j G_j
 
   const int chunk = blockIdx.x, hk = blockIdx.y;
   const int rep = p.hv / p.hk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
   const int64_t t0 = (int64_t)chunk * kC;
+  const int rt = tid >> 3, part = tid & 7;  // row-wise work: row rt, elements 16 part ..
+  const bool rvalid = t0 + rt < p.T;
+  const int64_t rrow = rvalid ? t0 + rt : p.T - 1;       // clamped, always a valid address
+  const int64_t lrow = t0 + lane < p.T ? t0 + lane : p.T - 1;
 
-  // q, k rows of the chunk (zero beyond T: such tokens have beta = 0, g = 0
-  // and leave the state unchanged); thread -> row tid/4, quarter tid%4, all
-  // loads issued before use; L2 norms reduced over the row's 4 threads
+  // the first head's v, beta, g go out with q and k
+  float vn[16], bn = 0.0f, gn = 0.0f;
+  auto load_head = [&](int h) {
+    load16<DT>(p.v, rrow * p.ld_v + (int64_t)h * kD + part * 16, vn);
+    bn = load_elem<DT>(p.beta, lrow * p.ld_beta + h);
+    gn = load_elem<DT>(p.g, lrow * p.ld_g + h);
+  };
+  load_head(hk * rep);
   {
-    const int t = tid >> 2, part = tid & 3;
-    const int64_t tt = t0 + t;
-    const bool valid = tt < p.T;
-    float kr[32], qr[32];
-    load32<DT>(p.k, tt * p.ld_k + (int64_t)hk * kD + part * 32, valid, kr);
-    load32<DT>(p.q, tt * p.ld_q + (int64_t)hk * kD + part * 32, valid, qr);
+    float kr[16], qr[16];
+    load16<DT>(p.k, rrow * p.ld_k + (int64_t)hk * kD + part * 16, kr);
+    load16<DT>(p.q, rrow * p.ld_q + (int64_t)hk * kD + part * 16, qr);
+    float ik = rvalid ? 1.0f : 0.0f, iq = ik;  // rows past T are zero
     if (p.normalize) {
       float sk2 = 0.0f, sq2 = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
+      for (int e = 0; e < 16; ++e) {
         sk2 += kr[e] * kr[e];
         sq2 += qr[e] * qr[e];
       }
-      sk2 += __shfl_xor(sk2, 1);
-      sk2 += __shfl_xor(sk2, 2);
-      sq2 += __shfl_xor(sq2, 1);
-      sq2 += __shfl_xor(sq2, 2);
-      const float ik = 1.0f / fmaxf(sqrtf(sk2), 1e-30f);
-      const float iq = 0.08838834764831845f / fmaxf(sqrtf(sq2), 1e-30f);  // 128^-1/2 / |q|
 #pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        kr[e] *= ik;
-        qr[e] *= iq;
+      for (int off = 1; off < 8; off <<= 1) {
+        sk2 += __shfl_xor(sk2, off);
+        sq2 += __shfl_xor(sq2, off);
       }
+      ik *= 1.0f / fmaxf(sqrtf(sk2), 1e-30f);
+      iq *= 0.08838834764831845f / fmaxf(sqrtf(sq2), 1e-30f);  // 128^-1/2 / |q|
     }
-    store32(&sk[t][part * 32], kr);
-    store32(&sq[t][part * 32], qr);
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      *reinterpret_cast<floatx4*>(&sk[rt][part * 16 + e]) =
+          floatx4{kr[e] * ik, kr[e + 1] * ik, kr[e + 2] * ik, kr[e + 3] * ik};
+      *reinterpret_cast<floatx4*>(&sq[rt][part * 16 + e]) =
+          floatx4{qr[e] * iq, qr[e + 1] * iq, qr[e + 2] * iq, qr[e + 3] * iq};
+    }
   }
   __syncthreads();
 
-  // k_t.k_j and q_t.k_j: thread -> row t, 16 columns, kept in registers for
-  // every value head of the group
-  const int mt = tid >> 2, j0 = (tid & 3) * 16;
-  float km[16], qm[16];
+  // K K^T (waves 0-3) or Q K^T (waves 4-7), rows 16 rb.., all 64 columns:
+  // gram[cb][r] = (X K^T)[16 rb + 4 lg + r][16 cb + li]
+  const int gmat = wave >> 2, rb = wave & 3;
+  floatx4 gram[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) km[i] = qm[i] = 0.0f;
-  for (int d = 0; d < kD; d += 4) {
-    const float4 kt = *reinterpret_cast<const float4*>(&sk[mt][d]);
-    const float4 qt = *reinterpret_cast<const float4*>(&sq[mt][d]);
+  for (int cb = 0; cb < 4; ++cb) gram[cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  {
+    const float* xrow = gmat ? &sq[16 * rb + li][0] : &sk[16 * rb + li][0];
+#pragma unroll 2
+    for (int k0 = 0; k0 < kD; k0 += 16) {
+      const floatx4 a = *reinterpret_cast<const floatx4*>(xrow + k0 + 4 * lg);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float4 kj = *reinterpret_cast<const float4*>(&sk[j0 + i][d]);
-      km[i] += kt.x * kj.x + kt.y * kj.y + kt.z * kj.z + kt.w * kj.w;
-      qm[i] += qt.x * kj.x + qt.y * kj.y + qt.z * kj.z + qt.w * kj.w;
+      for (int cb = 0; cb < 4; ++cb) {
+        const floatx4 b = *reinterpret_cast<const floatx4*>(&sk[16 * cb + li][k0 + 4 * lg]);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) gram[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s2], b[s2], gram[cb], 0, 0, 0);
+      }
     }
   }
 
   for (int hr = 0; hr < rep; ++hr) {
     const int h = hk * rep + hr;
     float* out = ws + ((int64_t)h * p.n_chunks + chunk) * kWsPerChunk;
-    if (wave == 0) {
-      const int64_t tt = t0 + lane;
-      float b = 0.0f, g = 0.0f;
-      if (tt < p.T) {
-        b = load_elem<DT>(p.beta, tt * p.ld_beta + h);
-        g = load_elem<DT>(p.g, tt * p.ld_g + h);
-      }
-      sbeta[lane] = b;
-      sgam[lane] = wave_prefix_sum(g, lane);
-    }
-    // this head's v rows, issued early
-    float vr[32];
-    {
-      const int t = tid >> 2, part = tid & 3;
-      load32<DT>(p.v, (t0 + t) * p.ld_v + (int64_t)h * kD + part * 32, t0 + t < p.T, vr);
-    }
-    __syncthreads();  // beta, gamma of this head; every read of the previous head's buffers done
-
-    // M[t][j] = beta_t exp(gam_t - gam_j) k_t.k_j (j < t) and
-    // A[t][j] = exp(gam_t - gam_j) q_t.k_j (j <= t)
+    __syncthreads();  // every read of the previous head's sv, sm, st, sgam, sbeta, scw is done
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = j0 + i;
-      const float dec = expf(sgam[mt] - sgam[j]);
-      sm[mt][j] = j < mt ? sbeta[mt] * dec * km[i] : 0.0f;
-      out[kWsA + mt * kC + j] = j <= mt ? dec * qm[i] : 0.0f;
+    for (int e = 0; e < 16; e += 4)
+      *reinterpret_cast<floatx4*>(&sv[rt][part * 16 + e]) =
+          rvalid ? floatx4{vn[e], vn[e + 1], vn[e + 2], vn[e + 3]} : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (wave == 0) {
+      const bool ok = t0 + lane < p.T;  // tokens past T: beta = 0, g = 0
+      const float b = ok ? bn : 0.0f;
+      const float gam = wave_prefix_sum(ok ? gn : 0.0f, lane);
+      sbeta[lane] = b;
+      sgam[lane] = gam;
+      scw[lane] = b * expf(gam);
     }
-    // diag(G) Q, diag(G_C / G) K, G_C, and the right-hand sides
-    // beta diag(G) K and beta V
+    __syncthreads();
+    // the next head's operands (the last head reloads itself) ahead of this
+    // head's stores
+    load_head(hr + 1 < rep ? h + 1 : h);
+
+    // M into LDS (waves 0-3), A out (waves 4-7)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * rb + 4 * lg + r;
+      const float gt = sgam[t], bt = sbeta[t];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int j = 16 * cb + li;
+        const float dec = expf(gt - sgam[j]);
+        if (gmat == 0)
+          sm[t][j] = j < t ? bt * dec * gram[cb][r] : 0.0f;
+        else
+          out[kWsA + t * kC + j] = j <= t ? dec * gram[cb][r] : 0.0f;
+      }
+    }
+    // diag(G) Q, diag(G_C / G) K, G_C
     const float gc = sgam[kC - 1];
     {
-      const int t = tid >> 2, part = tid & 3;
-      const float eg = expf(sgam[t]), egc = expf(gc - sgam[t]), bt = sbeta[t];
+      const float eg = expf(sgam[rt]), egc = expf(gc - sgam[rt]);
 #pragma unroll
-      for (int e = 0; e < 32; e += 4) {
-        const int d = part * 32 + e;
-        const float4 kv = *reinterpret_cast<const float4*>(&sk[t][d]);
-        const float4 qv = *reinterpret_cast<const float4*>(&sq[t][d]);
-        *reinterpret_cast<float4*>(out + kWsQ + t * kD + d) = make_float4(eg * qv.x, eg * qv.y, eg * qv.z, eg * qv.w);
-        *reinterpret_cast<float4*>(out + kWsK + t * kD + d) =
-            make_float4(egc * kv.x, egc * kv.y, egc * kv.z, egc * kv.w);
-        const float s = bt * eg;
-        *reinterpret_cast<float4*>(&sw[t][d]) = make_float4(s * kv.x, s * kv.y, s * kv.z, s * kv.w);
-        *reinterpret_cast<float4*>(&sv[t][d]) =
-            make_float4(bt * vr[e], bt * vr[e + 1], bt * vr[e + 2], bt * vr[e + 3]);
+      for (int e = 0; e < 16; e += 4) {
+        const floatx4 qv = *reinterpret_cast<const floatx4*>(&sq[rt][part * 16 + e]);
+        const floatx4 kv = *reinterpret_cast<const floatx4*>(&sk[rt][part * 16 + e]);
+        *reinterpret_cast<floatx4*>(out + kWsQ + rt * kD + part * 16 + e) = qv * eg;
+        *reinterpret_cast<floatx4*>(out + kWsK + rt * kD + part * 16 + e) = kv * egc;
       }
     }
     if (tid == 0) out[kWsG] = expf(gc);
-    __syncthreads();
+    __syncthreads();  // M complete
 
-    // [Wt | Ut] = (I + M)^-1 [rhs] by forward substitution in place: thread c
-    // owns column c of [sw | sv] (a wave's columns are all of one kind); 16
-    // rows at a time in registers, earlier rows read back final from LDS, M
-    // read as a broadcast
+    // diagonal blocks of T: lane (block i, column c) solves (I + M_ii) x = e_c
+    if (wave == 0) {
+      const int i = lane >> 4, c = lane & 15;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = r == c ? 1.0f : 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < r; ++jj) v -= sm[16 * i + r][16 * i + jj] * x[jj];
+        x[r] = v;
+        st[16 * i + r][16 * i + c] = v;
+      }
+    }
+    __syncthreads();
+    // off-diagonal blocks, one block diagonal d at a time: T_ij = -T_ii X,
+    // X = sum_{k=j}^{i-1} M_ik T_kj
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      if (wave < 4 - d) {
+        const int i = wave + d, j = wave;
+        floatx4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb = j; kb < i; ++kb) {
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&sm[16 * i + li][16 * kb + 4 * lg]);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s2], st[16 * kb + 4 * lg + s2][16 * j + li], x, 0, 0, 0);
+        }
+        floatx4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+        const floatx4 a = *reinterpret_cast<const floatx4*>(&st[16 * i + li][16 * i + 4 * lg]);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) y = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s2], x[s2], y, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[16 * i + 4 * lg + r][16 * j + li] = -y[r];
+      }
+      __syncthreads();
+    }
+
+    // Wt = T diag(beta G) K (waves 0-3), Ut = T diag(beta) V (waves 4-7);
+    // wave w owns column blocks 2(w%4), 2(w%4)+1, all four row blocks
     {
-      const bool wcol = tid < kD;
-      const int cc = tid & (kD - 1);
-      float* col = wcol ? &sw[0][cc] : &sv[0][cc];  // element t at col[t * kP]
-      for (int b0 = 0; b0 < kC; b0 += 16) {
-        float r[16];
+      const int pm = wave >> 2, cb0 = 32 * (wave & 3);
+      const float(*src)[kP] = pm ? sv : sk;
+      const float* coef = pm ? sbeta : scw;
+      float* dst = out + (pm ? kWsU : kWsW);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) r[i] = col[(b0 + i) * kP];
-        for (int j = 0; j < b0; j += 4) {  // b0 is a multiple of 16
-          const float y0 = col[j * kP], y1 = col[(j + 1) * kP], y2 = col[(j + 2) * kP], y3 = col[(j + 3) * kP];
+      for (int i = 0; i < 4; ++i) {
+        floatx4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int jb = 0; jb <= i; ++jb) {
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&st[16 * i + li][16 * jb + 4 * lg]);
+          const floatx4 cf = *reinterpret_cast<const floatx4*>(&coef[16 * jb + 4 * lg]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float4 m = *reinterpret_cast<const float4*>(&sm[b0 + i][j]);
-            r[i] -= m.x * y0 + m.y * y1 + m.z * y2 + m.w * y3;
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const int j = 16 * jb + 4 * lg + s2;
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s2], cf[s2] * src[j][cb0 + li], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s2], cf[s2] * src[j][cb0 + 16 + li], acc1, 0, 0, 0);
           }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-#pragma unroll
-          for (int jj = 0; jj < i; ++jj) r[i] -= sm[b0 + i][b0 + jj] * r[jj];
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * i + 4 * lg + r;
+          dst[t * kD + cb0 + li] = acc0[r];
+          dst[t * kD + cb0 + 16 + li] = acc1[r];
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) col[(b0 + i) * kP] = r[i];
       }
-      float* dst = out + (wcol ? kWsW : kWsU);
-      for (int t = 0; t < kC; ++t) dst[t * kD + cc] = col[t * kP];
     }
   }
 }
@@ -428,9 +463,9 @@ size_t gdn_workspace_floats(int64_t T, int hv) {
 hipError_t launch_gdn(const GdnArgs& p, float* ws, hipStream_t s) {
   const dim3 prep((unsigned)p.n_chunks, (unsigned)p.hk);
   if (p.in_dtype == NVFP4_DTYPE_BF16)
-    gdn_prep_kernel<NVFP4_DTYPE_BF16><<<prep, kThreads, 0, s>>>(p, ws);
+    gdn_prep_kernel<NVFP4_DTYPE_BF16><<<prep, kPrepThreads, 0, s>>>(p, ws);
   else
-    gdn_prep_kernel<NVFP4_DTYPE_F32><<<prep, kThreads, 0, s>>>(p, ws);
+    gdn_prep_kernel<NVFP4_DTYPE_F32><<<prep, kPrepThreads, 0, s>>>(p, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nsl = kD / kSlice;

@@ -70,7 +70,7 @@ struct RawBlock {
 struct BlockWalk {
   int64_t r, j, bpr, rows;
   int64_t dr, dj;
-  __device__ BlockWalk(int64_t rows_, int64_t bpr_) : rows(rows_), bpr(bpr_) {
+  __device__ BlockWalk(int64_t rows_, int64_t bpr_) : bpr(bpr_), rows(rows_) {
     const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     r = start / bpr;
