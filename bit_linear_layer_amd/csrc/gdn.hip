@@ -50,7 +50,7 @@ constexpr int64_t kWsW = 0;                  // Wt   [64][128]
 constexpr int64_t kWsU = kWsW + kC * kD;     // Ut   [64][128]
 constexpr int64_t kWsA = kWsU + kC * kD;     // A    [64][64]
 constexpr int64_t kWsQ = kWsA + kC * kC;     // diag(G) Q        [64][128]
-constexpr int64_t kWsK = kWsQ + kC * kD;     // diag(G_C / G) K  [64][128]
+constexpr int64_t kWsK = kWsQ + kC * kD;     // (diag(G_C / G) K)^T  [128][64]
 constexpr int64_t kWsG = kWsK + kC * kD;     // G_C (one float, padded to 4)
 constexpr int64_t kWsPerChunk = kWsG + 4;
 
@@ -123,6 +123,7 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
   __shared__ __attribute__((aligned(16))) float sgam[kC];     // cumulative log decay
   __shared__ __attribute__((aligned(16))) float sbeta[kC];    // beta_j
   __shared__ __attribute__((aligned(16))) float scw[kC];      // beta_j G_j
+  __shared__ __attribute__((aligned(16))) float segc[kC];     // G_C / G_t
 
   const int chunk = blockIdx.x, hk = blockIdx.y;
   const int rep = p.hv / p.hk;
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
       sbeta[lane] = b;
       sgam[lane] = gam;
       scw[lane] = b * expf(gam);
+      segc[lane] = expf(__shfl(gam, 63) - gam);
     }
     __syncthreads();
     // the next head's operands (the last head reloads itself) ahead of this
@@ -228,16 +230,23 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
           out[kWsA + t * kC + j] = j <= t ? dec * gram[cb][r] : 0.0f;
       }
     }
-    // diag(G) Q, diag(G_C / G) K, G_C
+    // diag(G) Q, (diag(G_C / G) K)^T (key dimension major: the scan reads it
+    // down the token axis), G_C
     const float gc = sgam[kC - 1];
     {
-      const float eg = expf(sgam[rt]), egc = expf(gc - sgam[rt]);
+      const float eg = expf(sgam[rt]);
 #pragma unroll
       for (int e = 0; e < 16; e += 4) {
         const floatx4 qv = *reinterpret_cast<const floatx4*>(&sq[rt][part * 16 + e]);
-        const floatx4 kv = *reinterpret_cast<const floatx4*>(&sk[rt][part * 16 + e]);
         *reinterpret_cast<floatx4*>(out + kWsQ + rt * kD + part * 16 + e) = qv * eg;
-        *reinterpret_cast<floatx4*>(out + kWsK + rt * kD + part * 16 + e) = kv * egc;
+      }
+      const int d = tid >> 2, tq = (tid & 3) * 16;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const int t = tq + e;
+        *reinterpret_cast<floatx4*>(out + kWsK + d * kC + t) =
+            floatx4{segc[t] * sk[t][d], segc[t + 1] * sk[t + 1][d], segc[t + 2] * sk[t + 2][d],
+                    segc[t + 3] * sk[t + 3][d]};
       }
     }
     if (tid == 0) out[kWsG] = expf(gc);
@@ -314,14 +323,14 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
 // One workgroup per (value head, 32-row slice of S); chunks in order.  The
 // three products of a chunk run on v_mfma_f32_16x16x4f32 (fp32 in, fp32
 // accumulate; lane l supplies A[l%16][l/16] and B[l/16][l%16] and holds
-// D[4(l/16)+r][l%16]):
+// D[4(l/16)+r][l%16]); inside each 16-wide K block lane group l/16 takes
+// k = 4(l/16) + s at step s, so operands are 16-byte LDS reads (U is kept
+// transposed, K^ arrives transposed):
 //   wave w: P = Wt S^T and O = diag(G) Q S^T for the 16x16 tile
 //           (t: 16(w/2).., c: 16(w%2)..), U = Ut - P, then O += A U;
 //   wave w: S[c][16w..16w+15] = G_C S + U^T diag(G_C/G) K for both 16-row
 //           halves of the slice.
 // The next chunk's data is loaded into registers while one is computed.
-constexpr int kPK = kD + 16;        // k rows, read down a column by 4 lane groups
-constexpr int kPU = kSlice + 16;    // U tile [64][32]
 
 // A chunk's data in registers: thread tid holds 4-float group number
 // tid + 512 i of Wt, diag(G) Q, diag(G_C/G) K ([64][128]) and of A
@@ -348,9 +357,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   __shared__ __attribute__((aligned(16))) float sS[kSlice][kP];  // this slice of the state
   __shared__ __attribute__((aligned(16))) float sW[kC][kP];      // Wt
   __shared__ __attribute__((aligned(16))) float sQ[kC][kP];      // diag(G) Q
-  __shared__ __attribute__((aligned(16))) float sK[kC][kPK];     // diag(G_C/G) K
+  __shared__ __attribute__((aligned(16))) float sKT[kD][kPA];    // (diag(G_C/G) K)^T
   __shared__ __attribute__((aligned(16))) float sA[kC][kPA];
-  __shared__ float sU[kC][kPU];
+  __shared__ __attribute__((aligned(16))) float sUT[kSlice][kPA];  // U^T: slice rows x tokens
 
   // workgroups of one head on one XCD (ids are dealt to the 8 XCDs
   // round-robin), so its slices share the L2 copy of the chunk data
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
       const int rr = f / (kD / 4), cc = (f % (kD / 4)) * 4;
       *reinterpret_cast<floatx4*>(&sW[rr][cc]) = nw[i];
       *reinterpret_cast<floatx4*>(&sQ[rr][cc]) = nq[i];
-      *reinterpret_cast<floatx4*>(&sK[rr][cc]) = nk[i];
+      *reinterpret_cast<floatx4*>(&sKT[f / (kC / 4)][(f % (kC / 4)) * 4]) = nk[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -403,21 +412,31 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
     scan_load(base + (int64_t)(chunk + 1 < p.n_chunks ? chunk + 1 : chunk) * kWsPerChunk, tid, uoff, nw, nq, nk, na,
               nu, ngc);
 
-    // P = Wt S^T and O = diag(G) Q S^T on this wave's tile
+    // P = Wt S^T and O = diag(G) Q S^T on this wave's tile; inside each
+    // 16-wide K block the lane group lk takes k = 4 lk + s at step s (any
+    // order of k gives the same sum), so each operand is one 16-byte read
     floatx4 accp = {0.0f, 0.0f, 0.0f, 0.0f}, acco = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-    for (int k = 0; k < kD / 4; ++k) {
-      const float bs = sS[16 * tj + li][4 * k + lk];
-      accp = __builtin_amdgcn_mfma_f32_16x16x4f32(sW[16 * ti + li][4 * k + lk], bs, accp, 0, 0, 0);
-      acco = __builtin_amdgcn_mfma_f32_16x16x4f32(sQ[16 * ti + li][4 * k + lk], bs, acco, 0, 0, 0);
-    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sU[16 * ti + 4 * lk + q][16 * tj + li] = cu[q] - accp[q];
+    for (int kb = 0; kb < kD / 16; ++kb) {
+      const floatx4 bs = *reinterpret_cast<const floatx4*>(&sS[16 * tj + li][16 * kb + 4 * lk]);
+      const floatx4 aw = *reinterpret_cast<const floatx4*>(&sW[16 * ti + li][16 * kb + 4 * lk]);
+      const floatx4 aq = *reinterpret_cast<const floatx4*>(&sQ[16 * ti + li][16 * kb + 4 * lk]);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        accp = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[s2], bs[s2], accp, 0, 0, 0);
+        acco = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[s2], bs[s2], acco, 0, 0, 0);
+      }
+    }
+    *reinterpret_cast<floatx4*>(&sUT[16 * tj + li][16 * ti + 4 * lk]) =
+        floatx4{cu[0] - accp[0], cu[1] - accp[1], cu[2] - accp[2], cu[3] - accp[3]};
     __syncthreads();
-    // O += A U over the key positions j <= t (A is lower triangular)
-    for (int k = 0; k < 4 * (ti + 1); ++k)
-      acco = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * ti + li][4 * k + lk], sU[4 * k + lk][16 * tj + li], acco,
-                                                  0, 0, 0);
+    // O += A U over key blocks kb <= ti (A is lower triangular)
+    for (int kb = 0; kb <= ti; ++kb) {
+      const floatx4 aa = *reinterpret_cast<const floatx4*>(&sA[16 * ti + li][16 * kb + 4 * lk]);
+      const floatx4 bu = *reinterpret_cast<const floatx4*>(&sUT[16 * tj + li][16 * kb + 4 * lk]);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acco = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[s2], bu[s2], acco, 0, 0, 0);
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t tt = (int64_t)chunk * kC + 16 * ti + 4 * lk + q;
@@ -437,10 +456,13 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
       floatx4 acc;
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = cgc * sS[16 * tc + 4 * lk + q][16 * wave + li];
-#pragma unroll 8
-      for (int k = 0; k < kC / 4; ++k)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sU[4 * k + lk][16 * tc + li], sK[4 * k + lk][16 * wave + li], acc,
-                                                   0, 0, 0);
+#pragma unroll
+      for (int kb = 0; kb < kC / 16; ++kb) {
+        const floatx4 au = *reinterpret_cast<const floatx4*>(&sUT[16 * tc + li][16 * kb + 4 * lk]);
+        const floatx4 bk = *reinterpret_cast<const floatx4*>(&sKT[16 * wave + li][16 * kb + 4 * lk]);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(au[s2], bk[s2], acc, 0, 0, 0);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) sS[16 * tc + 4 * lk + q][16 * wave + li] = acc[q];
     }
