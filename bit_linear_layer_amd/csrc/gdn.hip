@@ -336,15 +336,23 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
 // tid + 512 i of Wt, diag(G) Q, diag(G_C/G) K ([64][128]) and of A
 // ([64][64]), and the 4 elements of Ut its wave's U tile needs.  Native
 // vector types: arrays of HIP's float4 class stay in scratch memory.
-__device__ __attribute__((always_inline)) inline void scan_load(const float* in, int tid, int uoff, floatx4 (&w)[4],
-                                                                  floatx4 (&q)[4], floatx4 (&k)[4], floatx4 (&a)[2],
-                                                                  float (&u)[4], float& gc) {
+// A chunk's data in registers, in two halves loaded at different points:
+// Wt and diag(G) Q (read by the first phase of a step), and K^T, A, the
+// lane's Ut elements and G_C (read by the second).  Thread tid holds 4-float
+// groups tid + 512 i of each array.  Native vector types: arrays of HIP's
+// float4 class stay in scratch memory.
+__device__ __attribute__((always_inline)) inline void scan_load_wq(const float* in, int tid, floatx4 (&w)[4],
+                                                                     floatx4 (&q)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     w[i] = reinterpret_cast<const floatx4*>(in + kWsW)[tid + i * kScanThreads];
     q[i] = reinterpret_cast<const floatx4*>(in + kWsQ)[tid + i * kScanThreads];
-    k[i] = reinterpret_cast<const floatx4*>(in + kWsK)[tid + i * kScanThreads];
   }
+}
+__device__ __attribute__((always_inline)) inline void scan_load_ka(const float* in, int tid, int uoff, floatx4 (&k)[4],
+                                                                     floatx4 (&a)[2], float (&u)[4], float& gc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) k[i] = reinterpret_cast<const floatx4*>(in + kWsK)[tid + i * kScanThreads];
 #pragma unroll
   for (int i = 0; i < 2; ++i) a[i] = reinterpret_cast<const floatx4*>(in + kWsA)[tid + i * kScanThreads];
 #pragma unroll
@@ -374,27 +382,25 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   const int ti = wave >> 1, tj = wave & 1;  // U / O tile
   const int row0 = sl * kSlice;
   const float* base = ws + (int64_t)h * p.n_chunks * kWsPerChunk;
+  const int last = p.n_chunks - 1;
 
   const int uoff = (16 * ti + 4 * lk) * kD + row0 + 16 * tj + li;  // this lane's Ut elements
   floatx4 nw[4], nq[4], nk[4], na[2];
   float nu[4], ngc;
-  float cu[4], cgc;
 
-  for (int i = tid; i < kSlice * kD; i += kScanThreads) {
-    const int c = i / kD, d = i % kD;
-    sS[c][d] = p.s0 != nullptr ? p.s0[((int64_t)h * kD + row0 + c) * kD + d] : 0.0f;
-  }
-  scan_load(base, tid, uoff, nw, nq, nk, na, nu, ngc);
-
-  for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
-    // this chunk's data: registers -> LDS (every read of the previous
-    // chunk's data is behind the barrier at the end of the iteration)
+  auto put_wq = [&]() {  // Wt, diag(G) Q registers -> LDS
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int f = tid + i * kScanThreads;
       const int rr = f / (kD / 4), cc = (f % (kD / 4)) * 4;
       *reinterpret_cast<floatx4*>(&sW[rr][cc]) = nw[i];
       *reinterpret_cast<floatx4*>(&sQ[rr][cc]) = nq[i];
+    }
+  };
+  auto put_ka = [&]() {  // K^T, A registers -> LDS
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = tid + i * kScanThreads;
       *reinterpret_cast<floatx4*>(&sKT[f / (kC / 4)][(f % (kC / 4)) * 4]) = nk[i];
     }
 #pragma unroll
@@ -402,16 +408,27 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
       const int f = tid + i * kScanThreads;
       *reinterpret_cast<floatx4*>(&sA[f / (kC / 4)][(f % (kC / 4)) * 4]) = na[i];
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cu[r] = nu[r];
-    cgc = ngc;
-    __syncthreads();
-    // the next chunk's loads fly while this one is computed; unconditional
-    // (the last chunk reloads itself): a load under a branch makes the
-    // compiler wait for it where the paths join
-    scan_load(base + (int64_t)(chunk + 1 < p.n_chunks ? chunk + 1 : chunk) * kWsPerChunk, tid, uoff, nw, nq, nk, na,
-              nu, ngc);
+  };
 
+  for (int i = tid; i < kSlice * kD; i += kScanThreads) {
+    const int c = i / kD, d = i % kD;
+    sS[c][d] = p.s0 != nullptr ? p.s0[((int64_t)h * kD + row0 + c) * kD + d] : 0.0f;
+  }
+  scan_load_wq(base, tid, nw, nq);
+  scan_load_ka(base, tid, uoff, nk, na, nu, ngc);
+  put_wq();
+  __syncthreads();
+
+  // Two barriers per chunk.  Phase 1 reads Wt, diag(G) Q and S; phase 2
+  // reads A, K^T, U and writes S.  So K^T and A of this chunk go to LDS at
+  // the end of phase 1 and Wt, diag(G) Q of the next chunk at the end of
+  // phase 2, each half loaded into registers one phase earlier.  Loads are
+  // unconditional (the last chunk reloads itself): a load under a branch
+  // makes the compiler wait for it where the paths join.
+  for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
+    const float* nxt = base + (int64_t)min(chunk + 1, last) * kWsPerChunk;
+    // ---- phase 1
+    scan_load_wq(nxt, tid, nw, nq);
     // P = Wt S^T and O = diag(G) Q S^T on this wave's tile; inside each
     // 16-wide K block the lane group lk takes k = 4 lk + s at step s (any
     // order of k gives the same sum), so each operand is one 16-byte read
@@ -428,8 +445,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
       }
     }
     *reinterpret_cast<floatx4*>(&sUT[16 * tj + li][16 * ti + 4 * lk]) =
-        floatx4{cu[0] - accp[0], cu[1] - accp[1], cu[2] - accp[2], cu[3] - accp[3]};
-    __syncthreads();
+        floatx4{nu[0] - accp[0], nu[1] - accp[1], nu[2] - accp[2], nu[3] - accp[3]};
+    put_ka();
+    __syncthreads();  // U, K^T, A of this chunk in LDS; every read of Wt, Q, S done
+    // ---- phase 2
+    const float gc = ngc;
+    scan_load_ka(nxt, tid, uoff, nk, na, nu, ngc);
     // O += A U over key blocks kb <= ti (A is lower triangular)
     for (int kb = 0; kb <= ti; ++kb) {
       const floatx4 aa = *reinterpret_cast<const floatx4*>(&sA[16 * ti + li][16 * kb + 4 * lk]);
@@ -449,13 +470,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
       }
     }
     // S[c][16w + j] = G_C S + U^T diag(G_C/G) K: each wave reads and writes
-    // only its own 16 columns of the slice, after every wave's reads of S
-    // above (the barrier after U)
+    // only its own 16 columns of the slice
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc) {
       floatx4 acc;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = cgc * sS[16 * tc + 4 * lk + q][16 * wave + li];
+      for (int q = 0; q < 4; ++q) acc[q] = gc * sS[16 * tc + 4 * lk + q][16 * wave + li];
 #pragma unroll
       for (int kb = 0; kb < kC / 16; ++kb) {
         const floatx4 au = *reinterpret_cast<const floatx4*>(&sUT[16 * tc + li][16 * kb + 4 * lk]);
@@ -466,7 +486,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
 #pragma unroll
       for (int q = 0; q < 4; ++q) sS[16 * tc + 4 * lk + q][16 * wave + li] = acc[q];
     }
-    __syncthreads();  // every read of this chunk's data and of the new S is done
+    put_wq();         // the next chunk's Wt, diag(G) Q
+    __syncthreads();  // new S, next Wt and Q in LDS; every read of this chunk's A, K^T, U done
   }
   if (p.s_final != nullptr)
     for (int i = tid; i < kSlice * kD; i += kScanThreads) {
