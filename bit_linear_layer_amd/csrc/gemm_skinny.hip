@@ -121,9 +121,14 @@ void skinny_kernel(const GemmArgs p, int n_lo, int n_hi, int groups_per_block) {
   };
 
   __builtin_amdgcn_sched_barrier(0);  // copy offsets are ready before any load
-  // Activations: this wave's K slice of the M rows, loaded first, decoded
-  // once after the first three weight copies are in flight (vmcnt counts in
-  // issue order, so the decode waits only for these loads).
+  // The weight stream starts first; then this wave's K slice of the
+  // activation rows, decoded once into registers (the decode waits for the
+  // three copies as well: vmcnt counts in issue order).
+  // (the grid gives every workgroup at least one group: g_begin < g_end)
+  issue(g_begin, 0);
+  issue(g_begin + 1, 1);
+  issue(g_begin + 2, 2);
+  __builtin_amdgcn_sched_barrier(0);  // keep the copies ahead of the activation loads
   u32x4 a_c[QPW];
   uint32_t a_s[QPW];
   const bool live = r16 < p.M;
@@ -138,11 +143,6 @@ void skinny_kernel(const GemmArgs p, int n_lo, int n_hi, int groups_per_block) {
       a_s[qi] = *reinterpret_cast<const uint16_t*>(srow + (in ? (k0 >> 4) : 0));
     }
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the copies
-  // (the grid gives every workgroup at least one group: g_begin < g_end)
-  issue(g_begin, 0);
-  issue(g_begin + 1, 1);
-  issue(g_begin + 2, 2);
   half8 areg[QPW][4];
 #pragma unroll
   for (int qi = 0; qi < QPW; ++qi) {
