@@ -69,6 +69,20 @@ def test_exact_and_near_midpoints_non_power_of_two_scale(g):
     assert_quant_exact(xt, quantize_dev(xt, float(g)), g=g)
 
 
+@pytest.mark.parametrize("mag", [1e-30, 1e-39])
+def test_tiny_magnitudes(mag):
+    """float32 inputs so small that s * g lies below 2^-90 (the kernel's
+    exact threshold count instead of its bracketed hardware pack); at 1e-39
+    the inputs and the global scale are subnormal."""
+    say(f"quantize tiny magnitudes {mag}")
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((8, 64)) * mag).astype(np.float32)
+    xt = torch.from_numpy(x).to(DEV)
+    assert_quant_exact(xt, quantize_dev(xt))
+    gs = float(np.float32(mag * 0.01))
+    assert_quant_exact(xt, quantize_dev(xt, gs), g=np.float32(gs))
+
+
 def test_static_scale_saturation():
     """A too-small calibrated scale saturates block scales at 448 and
     elements at 6."""
