@@ -597,6 +597,7 @@ hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
 using CfgL = TileCfg<256, 256, 4, 2, 7>;
 using CfgM = TileCfg<128, 128, 2, 2, 0>;  // medium shapes / better wave fill
 using CfgS = TileCfg<32, 128, 1, 4, 0>;   // M <= 32
+using CfgH = TileCfg<256, 128, 4, 2, 7>;  // the columns past whole waves of CfgL tiles
 
 double fill(int64_t tiles) {
   const int64_t waves = (tiles + 255) / 256;
@@ -613,7 +614,24 @@ hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStr
   if (p.M <= 32) return launch_cfg<CfgS, kEpiPlain>(p, n_lo, n_hi, s);
   const int64_t tl = (int64_t)((p.M + 255) / 256) * ((n + 255) / 256);
   const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((n + 127) / 128);
-  if (p.M >= 256 && n >= 256 && fill(tl) >= 0.8 * fill(tmd)) return launch_cfg<CfgL, kEpiPlain>(p, n_lo, n_hi, s);
+  if (p.M >= 256 && n >= 256 && fill(tl) >= 0.8 * fill(tmd)) {
+    // A partly filled last wave of 256x256 tiles: keep whole waves of them
+    // on the leading columns and cover the rest with 256x128 tiles, a wave
+    // of half-size work instead of a half-empty wave (two launches on the
+    // stream; every output column still sees its whole K).
+    const int64_t tm = (p.M + 255) / 256;
+    if (fill(tl) < 0.9) {
+      for (int k = n / 256 - 1; k > 0; --k) {
+        if ((tm * k) % 256 != 0) continue;
+        const int rest = n - 256 * k;
+        if (fill(tm * ((rest + 127) / 128)) < 0.9) continue;
+        const hipError_t e = launch_cfg<CfgL, kEpiPlain>(p, n_lo, n_lo + 256 * k, s);
+        if (e != hipSuccess) return e;
+        return launch_cfg<CfgH, kEpiPlain>(p, n_lo + 256 * k, n_hi, s);
+      }
+    }
+    return launch_cfg<CfgL, kEpiPlain>(p, n_lo, n_hi, s);
+  }
   return launch_cfg<CfgM, kEpiPlain>(p, n_lo, n_hi, s);
 }
 
