@@ -20,7 +20,8 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  Host
  *     arrays and structs are read only during the call.  The library
- *     allocates no memory and keeps no mutable global state.
+ *     allocates no memory; its only global state is the device's compute
+ *     unit count, queried once per process to size the small-M GEMM grid.
  *   - Every call enqueues work on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and returns without synchronizing.
  *   - Matrices are row-major.  An NVFP4 matrix [rows, cols] is:
