@@ -1,8 +1,9 @@
 // Exact NVFP4 quantization of one 16-element block, shared by the quantize
 // pass and the GEMM epilogue that quantizes its own output.  Blocks take a
 // bracketed path on the hardware E2M1 pack with an exact per-element repair
-// (quantize_block16); scales outside float32's comfortable range take the
-// threshold count below.
+// (quantize_block16), and the block scale a bracketed path on the hardware
+// E4M3 conversion (block_scale_code); scales outside float32's comfortable
+// range take the threshold count and the float64 division below.
 //
 // Format (evolve.pub review of arXiv 2609.04098, "Scope & Claims";
 // thevalue.engineering article, section on the fragility myth): E2M1 codes
@@ -16,10 +17,10 @@
 // tie goes up.  mu * s * g <= 3 + 4 + 24 = 31 bits is an exact float64
 // number; |x| is a float32, so "|x| > t" is "|x| >= the next float32 above
 // t" and "|x| >= t" is "|x| >= the smallest float32 not below t" -- one exact
-// float32 bound per threshold and block.  The block scale is one correctly rounded float64
-// division amax_b / (6 g): a non-tie quotient lies >= 2^-31 (relative) from
-// every E4M3 midpoint, far above float64's 2^-53 rounding, so rounding the
-// float64 quotient to E4M3 is exact.
+// float32 bound per threshold and block.  The float64 form of the block
+// scale is one correctly rounded division amax_b / (6 g): a non-tie quotient
+// lies >= 2^-31 (relative) from every E4M3 midpoint, far above float64's
+// 2^-53 rounding, so rounding the float64 quotient to E4M3 is exact.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -85,6 +86,33 @@ __device__ inline float e4m3_value_f32(uint32_t code) {
   return code < 8u ? (float)code * 0x1p-9f : __uint_as_float((code + (120u << 3)) << 20);
 }
 
+// E4M3 code of the block scale: the nearest E4M3 value to the exact real
+// amax_b / (6 g), ties to the even code, saturating at 448, 0 for a zero
+// block or g = 0.  Bracketed like the elements: fl32(6 g) and its hardware
+// reciprocal widened by 2^-18 each way put two float32 products on either
+// side of the exact quotient; clamped to 448 (the saturating rule's own
+// answer) both go through gfx950's E4M3 conversion (nearest, ties to even,
+// subnormals included).  Equal codes are exact; otherwise the quotient is
+// next to the midpoint mu of the two candidate values, and
+// fma(6 mu, g, -amax_b) decides (6 mu has <= 7 bits; with 6 g in
+// [2^-80, 2^100] a nonzero difference is a normal float32; zero is a tie,
+// which goes to the even code).  Outside that range: one correctly rounded
+// float64 division (exact by the bit counts above).
+__device__ inline uint32_t block_scale_code(float amax_b, float g) {
+  if (g == 0.0f || amax_b == 0.0f) return 0u;
+  const float d6 = 6.0f * g;
+  if (!(d6 >= 0x1p-80f && d6 <= 0x1p100f)) return e4m3_rne((double)amax_b / (6.0 * (double)g));  // 6 g is exact
+  const float r = __builtin_amdgcn_rcpf(d6);
+  const float q_lo = fminf(amax_b * (r * (1.0f - 0x1p-18f)), 448.0f);
+  const float q_hi = fminf(amax_b * (r * (1.0f + 0x1p-18f)), 448.0f);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q_lo, q_hi, 0, false);
+  const uint32_t lo = w & 0xFFu, hi = (w >> 8) & 0xFFu;
+  if (lo == hi) return lo;
+  const float mu6 = 3.0f * (e4m3_value_f32(lo) + e4m3_value_f32(hi));  // 6 * midpoint, exact
+  const float d = fmaf(mu6, g, -amax_b);
+  return (d < 0.0f || (d == 0.0f && (lo & 1u))) ? hi : lo;
+}
+
 // Byte P of lo / hi <- E2M1 codes of (a, b) times r_lo / r_hi (a in the low nibble).
 template <int P>
 __device__ inline void pack_pair(uint32_t& lo, uint32_t& hi, float a, float b, float r_lo, float r_hi) {
@@ -119,9 +147,7 @@ __device__ inline uint32_t quantize_block16(const float v[16], float g, uint2* c
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax_b = fmaxf(amax_b, fabsf(v[i]));
 
-  uint32_t s = 0;
-  if (g != 0.0f && amax_b != 0.0f) s = e4m3_rne((double)amax_b / (6.0 * (double)g));  // 6 g is exact
-
+  const uint32_t s = block_scale_code(amax_b, g);
   const float sv = e4m3_value_f32(s);
   const float S = sv * g;
   if (s != 0u && !(S >= 0x1p-90f && S <= 0x1p126f)) {

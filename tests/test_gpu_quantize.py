@@ -69,6 +69,25 @@ def test_exact_and_near_midpoints_non_power_of_two_scale(g):
     assert_quant_exact(xt, quantize_dev(xt, float(g)), g=g)
 
 
+def test_block_scale_midpoints():
+    """Blocks whose amax is 6 g times an E4M3 midpoint (exactly, and one
+    float32 step either side): the block scale's rounding decision itself
+    sits on or next to a tie (the kernel's bracketed scale path and its
+    exact repair)."""
+    say("quantize block-scale midpoints")
+    g = np.float32(0.8125 * 2.0 ** -5)
+    vals = O.E4M3_VALUES[:0x7F]
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    am = (6.0 * float(g) * mids).astype(np.float32)
+    am = np.concatenate([am, np.nextafter(am, np.float32(np.inf)), np.nextafter(am, np.float32(0))])
+    rng = np.random.default_rng(21)
+    x = (rng.uniform(-1, 1, (am.size, 16)) * am[:, None]).astype(np.float32)
+    x[np.arange(am.size), rng.integers(0, 16, am.size)] = am * rng.choice([-1, 1], am.size).astype(np.float32)
+    x = x.reshape(-1, 64) if x.shape[0] % 4 == 0 else x[: x.shape[0] // 4 * 4].reshape(-1, 64)
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    assert_quant_exact(xt, quantize_dev(xt, float(g)), g=g)
+
+
 @pytest.mark.parametrize("mag", [1e-30, 1e-39])
 def test_tiny_magnitudes(mag):
     """float32 inputs so small that s * g lies below 2^-90 (the kernel's
