@@ -23,6 +23,11 @@
 //   16-byte read per lane, consecutive lanes consecutive addresses) and
 //   decodes them in registers: 4 x v_cvt_scalef32_pk_f16_fp4 + 4 x
 //   v_pk_mul_f16 per 8 elements; then v_mfma_f32_32x32x16_f16.
+//   Large shapes whose K is a whole number of K tiles run gemm_kernel_pipe:
+//   one wave per SIMD with 128x128 outputs each (a decoded fragment feeds
+//   four MFMAs), software-pipelined across K tiles; other shapes run
+//   gemm_kernel (two waves per SIMD for the 256-wide tiles, and the ragged
+//   last K tile through registers).
 //
 // K order inside a 128-wide K tile.  The MFMA sums over its 16 k values, so
 // any permutation of k that A and W share is allowed.  Lane (row, h) of a
@@ -31,6 +36,8 @@
 // and its scales are 4 contiguous bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_util.h"
 #include "internal.h"
@@ -124,7 +131,8 @@ struct AsyncLoader {
   int clds[kCodePer], slds[kScalePer];  // wave-uniform LDS offsets in the stage
   bool cB[kCodePer], sB[kScalePer];
 
-  __device__ void init(const GemmArgs& p, int m0, int n0, int n_hi, int wave, int lane) {
+  __device__ __attribute__((always_inline)) void init(const GemmArgs& p, int m0, int n0, int n_hi, int wave,
+                                                     int lane) {
     ra_c = buffer_rsrc(p.a_codes, (uint32_t)((int64_t)p.M * p.lda_c));
     ra_s = buffer_rsrc(p.a_scales, (uint32_t)((int64_t)p.M * p.lda_s));
     rw_c = buffer_rsrc(p.w_codes, (uint32_t)((int64_t)p.N * p.ldw_c));
@@ -160,15 +168,39 @@ struct AsyncLoader {
   // slots repeat group 0: identical bytes to identical LDS addresses), so
   // a fixed vmcnt tells how many tiles are still in flight.
   static constexpr int kPerTile = kCodePer + kScalePer;
-  __device__ void issue(uint8_t* stage, int kt) const {
-#pragma unroll
-    for (int i = 0; i < kCodePer; ++i)
-      llvm_amdgcn_raw_buffer_load_lds(cB[i] ? rw_c : ra_c, (lds_u32_ptr)(stage + clds[i]), 16, cvoff[i],
+  // Copy slot i alone (codes first, then scales): lets a caller spread one
+  // tile's copies over several points of its instruction stream.
+  __device__ __attribute__((always_inline)) void issue_slot(uint8_t* stage, int kt, int i) const {
+    if (i < kCodePer) {
+      const bool isB = kCodeSplit ? i * kWaves >= C::BM / 32 * 2 : cB[i];
+      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_c : ra_c, (lds_u32_ptr)(stage + clds[i]), 16, cvoff[i],
                                       kt * kRowCodeBytes, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kScalePer; ++i)
-      llvm_amdgcn_raw_buffer_load_lds(sB[i] ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[i]), 4, svoff[i],
+    } else {
+      const int j = i - kCodePer;
+      const bool isB = kScaleSplit ? j * kWaves >= C::BM / 32 : sB[j];
+      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[j]), 4, svoff[j],
                                       kt * kRowScaleBytes, 0, 0);
+    }
+  }
+
+  // When the waves split the A groups and all groups evenly (no idle
+  // slots), slot i's operand (A or W) is the same for every wave and known
+  // at compile time.
+  static constexpr bool kCodeSplit = (C::BM / 32 * 2) % kWaves == 0 && kCodeGroups % kWaves == 0;
+  static constexpr bool kScaleSplit = (C::BM / 32) % kWaves == 0 && kScaleGroups % kWaves == 0;
+  __device__ __attribute__((always_inline)) void issue(uint8_t* stage, int kt) const {
+#pragma unroll
+    for (int i = 0; i < kCodePer; ++i) {
+      const bool isB = kCodeSplit ? i * kWaves >= C::BM / 32 * 2 : cB[i];
+      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_c : ra_c, (lds_u32_ptr)(stage + clds[i]), 16, cvoff[i],
+                                      kt * kRowCodeBytes, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kScalePer; ++i) {
+      const bool isB = kScaleSplit ? i * kWaves >= C::BM / 32 : sB[i];
+      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[i]), 4, svoff[i],
+                                      kt * kRowScaleBytes, 0, 0);
+    }
   }
 };
 
@@ -372,6 +404,82 @@ __device__ __attribute__((always_inline)) inline void swiglu_epilogue(
   }
 }
 
+// The epilogue of one output tile from its accumulators: the gated-MLP
+// epilogue, or per output column its segment's global scale (and gate).
+template <class C, int EPI>
+__device__ __attribute__((always_inline)) inline void finish_tile(
+    const GemmArgs& p, floatx16 (&acc)[C::FM][C::FN], int m0, int n0, int n_hi, int fm0, int fn0, int wn,
+    int lane, uint8_t* smem) {
+  if constexpr (EPI == kEpiSwiglu) {
+    swiglu_epilogue<C>(p, acc, m0, n0, fm0, wn, lane, smem);
+    return;
+  }
+
+  const float ga = *p.ep.a_g;
+  float colscale[C::FN], alog[C::FN], dtb[C::FN];
+  int coln[C::FN], kind[C::FN];
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j) {
+    const int n = n0 + (fn0 + j) * 32 + (lane & 31);
+    coln[j] = n;
+    int seg = 0;
+    for (int s = 1; s < p.ep.n_seg; ++s) seg += (n >= p.ep.seg_off[s]) ? 1 : 0;
+    colscale[j] = ga * p.ep.seg_g[seg];
+    kind[j] = 0;
+    alog[j] = 0.0f;
+    dtb[j] = 0.0f;
+    if constexpr (EPI == kEpiGate) {
+      kind[j] = (seg == p.ep.b_seg) ? 1 : (seg == p.ep.a_seg ? 2 : 0);
+      if (kind[j] == 2 && n < n_hi) {
+        const int h = n - p.ep.seg_off[seg];
+        alog[j] = expf(p.ep.A_log[h]);
+        dtb[j] = p.ep.dt_bias[h];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = acc[i][j][r] * colscale[j];
+        if constexpr (EPI == kEpiGate) {
+          acc[i][j][r] = gate_value(x, kind[j], alog[j], dtb[j]);
+        } else {
+          acc[i][j][r] = x;
+        }
+      }
+  // bf16 output through LDS: the MFMA layout gives each lane one column of
+  // 16 rows, so direct stores are 2-byte scatters (one instruction per
+  // element); staged, every lane stores 16 contiguous bytes.
+  if (p.out_bf16 && p.ld_out % 8 == 0 && ((uintptr_t)p.out & 15) == 0 && n0 % 8 == 0) {
+    stage_bf16_and_store<C>(acc, fm0, fn0, lane, smem, m0, n0, p.M, n_hi,
+                            reinterpret_cast<uint16_t*>(p.out), p.ld_out);
+    return;
+  }
+  const bool full_tile = m0 + C::BM <= p.M && n0 + C::BN <= n_hi;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int mb = m0 + (fm0 + i) * 32 + 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int n = coln[j];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + (r & 3);
+        if (full_tile || (m < p.M && n < n_hi)) {
+          const float v = acc[i][j][r];
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.ld_out + n] = (uint16_t)f32_to_bf16_bits(v);
+          else
+            reinterpret_cast<float*>(p.out)[(int64_t)m * p.ld_out + n] = v;
+        }
+      }
+    }
+  }
+}
+
 // One launch covers the output columns [n_lo, n_hi).  EPI = kEpiGate is
 // launched only over the gate segments' columns, so the bulk of the output
 // runs gate-free code; kEpiSwiglu covers the columns of h.
@@ -503,78 +611,183 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
     compute_tile(st, [] {});
   }
 
-  if constexpr (EPI == kEpiSwiglu) {
-    swiglu_epilogue<C>(p, acc, m0, n0, fm0, wn, lane, smem);
-    return;
-  }
-
-  // Epilogue: per output column its segment's global scale (and gate).
-  const float ga = *p.ep.a_g;
-  float colscale[C::FN], alog[C::FN], dtb[C::FN];
-  int coln[C::FN], kind[C::FN];
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j) {
-    const int n = n0 + (fn0 + j) * 32 + (lane & 31);
-    coln[j] = n;
-    int seg = 0;
-    for (int s = 1; s < p.ep.n_seg; ++s) seg += (n >= p.ep.seg_off[s]) ? 1 : 0;
-    colscale[j] = ga * p.ep.seg_g[seg];
-    kind[j] = 0;
-    alog[j] = 0.0f;
-    dtb[j] = 0.0f;
-    if constexpr (EPI == kEpiGate) {
-      kind[j] = (seg == p.ep.b_seg) ? 1 : (seg == p.ep.a_seg ? 2 : 0);
-      if (kind[j] == 2 && n < n_hi) {
-        const int h = n - p.ep.seg_off[seg];
-        alog[j] = expf(p.ep.A_log[h]);
-        dtb[j] = p.ep.dt_bias[h];
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x = acc[i][j][r] * colscale[j];
-        if constexpr (EPI == kEpiGate) {
-          acc[i][j][r] = gate_value(x, kind[j], alog[j], dtb[j]);
-        } else {
-          acc[i][j][r] = x;
-        }
-      }
-  // bf16 output through LDS: the MFMA layout gives each lane one column of
-  // 16 rows, so direct stores are 2-byte scatters (one instruction per
-  // element); staged, every lane stores 16 contiguous bytes.
-  if (p.out_bf16 && p.ld_out % 8 == 0 && ((uintptr_t)p.out & 15) == 0 && n0 % 8 == 0) {
-    stage_bf16_and_store<C>(acc, fm0, fn0, lane, smem, m0, n0, p.M, n_hi,
-                            reinterpret_cast<uint16_t*>(p.out), p.ld_out);
-    return;
-  }
-  const bool full_tile = m0 + C::BM <= p.M && n0 + C::BN <= n_hi;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int mb = m0 + (fm0 + i) * 32 + 4 * (lane >> 5);
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int n = coln[j];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mb + 8 * (r >> 2) + (r & 3);
-        if (full_tile || (m < p.M && n < n_hi)) {
-          const float v = acc[i][j][r];
-          if (p.out_bf16)
-            reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.ld_out + n] = (uint16_t)f32_to_bf16_bits(v);
-          else
-            reinterpret_cast<float*>(p.out)[(int64_t)m * p.ld_out + n] = v;
-        }
-      }
-    }
-  }
+  finish_tile<C, EPI>(p, acc, m0, n0, n_hi, fm0, fn0, wn, lane, smem);
 }
 
+// Large shapes whose K is a whole number (>= 2) of 128-wide tiles: one wave
+// per SIMD, each owning 128x128 outputs (16 accumulator fragments, held in
+// the accumulation registers), so every decoded fragment feeds four MFMAs
+// and a k-step decodes 8 fragments for 16 MFMAs.  One wave per SIMD has no
+// second wave to cover its stalls, so the K loop is software-pipelined
+// across tiles: the codes of k-steps 4-7 are read from LDS during k-step 1,
+// the next tile's k-steps 0-3 and scales during k-step 4 (after the
+// workgroup barrier that certifies that tile's copies), and k-step 7
+// decodes the next tile's first k-step.  The LDS stage of tile kt is
+// rewritten (with tile kt+3) only after that barrier, which every wave
+// reaches after its last read of the stage.
 template <class C, int EPI>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
+  static_assert(C::kWavesPerSimd == 1, "one wave per SIMD");
+  static_assert((C::FM + C::FN) % C::FM == 0 && C::FN % ((C::FM + C::FN) / C::FM) == 0, "decode split");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tiles_m = (p.M + C::BM - 1) / C::BM;
+  constexpr int kCols = tile_cols<C, EPI>();
+  const int tiles_n = (n_hi - n_lo + kCols - 1) / kCols;
+  int tm, tn;
+  tile_of((int)blockIdx.x, (int)gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM, n0 = n_lo + tn * kCols;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int fm0 = wm * C::FM, fn0 = wn * C::FN;
+  constexpr int NF = C::FM + C::FN;  // fragments: A first, then W
+
+  floatx16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // This lane's code chunk (k-steps 0-3; +1024 bytes: 4-7) and scale dword
+  // of fragment f in a stage.
+  auto code_at = [&](const uint8_t* st, int f, int half) __attribute__((always_inline)) -> u32x4 {
+    const int off = f < C::FM ? (fm0 + f) * 2048 : C::kACode + (fn0 + f - C::FM) * 2048;
+    return *reinterpret_cast<const u32x4*>(st + off + half * 1024 + lane * 16);
+  };
+  auto scale_at = [&](const uint8_t* st, int f) __attribute__((always_inline)) -> uint32_t {
+    const int off = f < C::FM ? C::kACode + C::kBCode + (fm0 + f) * 256
+                              : C::kACode + C::kBCode + C::kAScale + (fn0 + f - C::FM) * 256;
+    return *reinterpret_cast<const uint32_t*>(st + off + lane * 4);
+  };
+
+  constexpr int kPer = AsyncLoader<C, EPI>::kPerTile;
+  const int nk = p.K / kBK;  // >= 2, K % 128 == 0 (checked by the launcher)
+  AsyncLoader<C, EPI> ld;
+  ld.init(p, m0, n0, n_hi, wave, lane);
+  // Every wave keeps exactly two tiles' copies in flight behind the one it
+  // waits for: past the last tile it re-copies the last tile (in bounds)
+  // into a stage nobody reads again, so the waits are the same every tile
+  // and the K loop has no branches.
+  ld.issue(smem, 0);
+  ld.issue(smem + C::kStage, 1);
+  ld.issue(smem + 2 * C::kStage, min(2, nk - 1));
+  wait_vmem<2 * kPer>();  // tile 0 landed
+  barrier_lds();
+
+  u32x4 c_lo[NF];
+  uint32_t sc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    c_lo[f] = code_at(smem, f, 0);
+    sc[f] = scale_at(smem, f);
+  }
+  half2v s2[NF];
+  half8 cur[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    s2[f] = scale_pair(sc[f], 0);
+    cur[f] = decode8(c_lo[f][0], s2[f]);
+  }
+
+  // One K tile; MORE: a next tile follows (its first k-step is decoded here).
+  auto tile = [&](int kt, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool MORE = decltype(more_tag)::value;
+    const uint8_t* st = smem + (kt % 3) * C::kStage;
+    u32x4 c_hi[NF], n_lo[NF];
+    uint32_t nsc[NF];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t == 1) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) c_hi[f] = code_at(st, f, 1);
+      }
+      if constexpr (MORE) {
+        if (t == 4) {
+          wait_vmem<kPer>();  // tile kt+1 landed, kt+2 may fly
+          barrier_lds();
+          // the barrier's lgkmcnt(0) again, visible to the compiler's own
+          // wait insertion (it cannot see inside the asm): the codes read
+          // before the barrier need no further wait
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          const uint8_t* nst = smem + ((kt + 1) % 3) * C::kStage;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            n_lo[f] = code_at(nst, f, 0);
+            nsc[f] = scale_at(nst, f);
+          }
+        }
+      }
+      // The k-step in FM regions, each scheduled as one unit: region r
+      // issues the MFMAs of accumulator row r interleaved with the decode of
+      // two fragments for the next k-step (W fragments first: every MFMA of
+      // the next step's first region needs all of them) and, in k-steps 4-7,
+      // one of the copies of tile kt+3 into this tile's stage.  Issued back
+      // to back, the copies stall the wave (and so its MFMAs) until the
+      // memory pipeline takes them.
+      const bool dec = t < 7 || MORE;
+      constexpr int kPerRegion = NF / C::FM;
+      constexpr int kPerStep = (kPer + 3) / 4;
+      half8 nxt[NF];
+#pragma unroll
+      for (int r = 0; r < C::FM; ++r) {
+        if (dec) {
+#pragma unroll
+          for (int q = 0; q < kPerRegion; ++q) {
+            const int e = r * kPerRegion + q;             // decode order
+            const int f = e < C::FN ? C::FM + e : e - C::FN;  // W fragments, then A
+            if (t < 7) {
+              const int u = t + 1;
+              if ((u & 1) == 0) s2[f] = scale_pair(sc[f], u >> 1);
+              nxt[f] = decode8(u < 4 ? c_lo[f][u] : c_hi[f][u - 4], s2[f]);
+            } else {
+              s2[f] = scale_pair(nsc[f], 0);
+              nxt[f] = decode8(n_lo[f][0], s2[f]);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[r], cur[C::FM + j], acc[r][j], 0, 0, 0);
+        if constexpr (MORE) {
+          if (t >= 4 && r < kPerStep && (t - 4) * kPerStep + r < kPer)
+            ld.issue_slot(smem + (kt % 3) * C::kStage, min(kt + 3, nk - 1), (t - 4) * kPerStep + r);
+        }
+        if (dec) {
+          if constexpr (C::kSchedValu > 0) {
+#pragma unroll
+            for (int g = 0; g < C::FN; ++g) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, C::kSchedValu, 0);  // VALU
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (dec) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
+      }
+    }
+    if constexpr (MORE) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        c_lo[f] = n_lo[f];
+        sc[f] = nsc[f];
+      }
+    }
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::true_type{});
+  tile(nk - 1, std::false_type{});
+  wait_vmem<0>();  // the re-copies have landed before the epilogue reuses LDS
+
+  finish_tile<C, EPI>(p, acc, m0, n0, n_hi, fm0, fn0, wn, lane, smem);
+}
+
+template <class C, int EPI, bool PIPE = false>
 hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
   constexpr int kCols = tile_cols<C, EPI>();
@@ -584,20 +797,34 @@ hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   const size_t tile = (size_t)C::BM * staged_row_bytes<kCols>();
   const size_t lds = 3 * (size_t)C::kStage > tile ? 3 * (size_t)C::kStage : tile;
   // raising the dynamic-LDS limit is idempotent and cheap
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<C, EPI>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const void* fn;
+  if constexpr (PIPE) fn = (const void*)gemm_kernel_pipe<C, EPI>;
+  else fn = (const void*)gemm_kernel<C, EPI>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  gemm_kernel<C, EPI><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p, n_lo, n_hi);
+  if constexpr (PIPE)
+    gemm_kernel_pipe<C, EPI><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p, n_lo, n_hi);
+  else
+    gemm_kernel<C, EPI><<<(unsigned)nblocks, C::kThreads, lds, s>>>(p, n_lo, n_hi);
   return hipGetLastError();
 }
 
-// Large prefill shapes: 8 waves, two per SIMD, so one wave's decode VALU
-// work runs while the other's MFMAs occupy the matrix core (measured: one
-// wave per SIMD barely overlaps its own decode with its MFMAs).
+// Large prefill shapes with a ragged last K tile: 8 waves, two per SIMD, so
+// one wave's decode VALU work runs while the other's MFMAs occupy the
+// matrix core.
 using CfgL = TileCfg<256, 256, 4, 2, 7>;
 using CfgM = TileCfg<128, 128, 2, 2, 0>;  // medium shapes / better wave fill
 using CfgS = TileCfg<32, 128, 1, 4, 0>;   // M <= 32
 using CfgH = TileCfg<256, 128, 4, 2, 7>;  // the columns past whole waves of CfgL tiles
+using CfgP = TileCfg<256, 256, 2, 2, 4>;  // CfgL's tiles, one wave per SIMD (gemm_kernel_pipe)
+
+// 256x256 tiles: the pipelined one-wave-per-SIMD kernel when K is a whole
+// number (>= 2) of K tiles, else the two-wave kernel with its tail path.
+template <int EPI>
+hipError_t launch_large(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
+  if (p.K % kBK == 0 && p.K >= 2 * kBK) return launch_cfg<CfgP, EPI, true>(p, n_lo, n_hi, s);
+  return launch_cfg<CfgL, EPI>(p, n_lo, n_hi, s);
+}
 
 double fill(int64_t tiles) {
   const int64_t waves = (tiles + 255) / 256;
@@ -625,12 +852,12 @@ hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStr
         if ((tm * k) % 256 != 0) continue;
         const int rest = n - 256 * k;
         if (fill(tm * ((rest + 127) / 128)) < 0.9) continue;
-        const hipError_t e = launch_cfg<CfgL, kEpiPlain>(p, n_lo, n_lo + 256 * k, s);
+        const hipError_t e = launch_large<kEpiPlain>(p, n_lo, n_lo + 256 * k, s);
         if (e != hipSuccess) return e;
         return launch_cfg<CfgH, kEpiPlain>(p, n_lo + 256 * k, n_hi, s);
       }
     }
-    return launch_cfg<CfgL, kEpiPlain>(p, n_lo, n_hi, s);
+    return launch_large<kEpiPlain>(p, n_lo, n_hi, s);
   }
   return launch_cfg<CfgM, kEpiPlain>(p, n_lo, n_hi, s);
 }
@@ -688,7 +915,7 @@ hipError_t launch_gemm_swiglu(const GemmArgs& p, hipStream_t s) {
   const int64_t tl = (int64_t)((p.M + 255) / 256) * ((inter + 127) / 128);
   const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((inter + 63) / 64);
   if (p.M >= 256 && inter >= 128 && fill(tl) >= 0.8 * fill(tmd))
-    return launch_cfg<CfgL, kEpiSwiglu>(p, 0, inter, s);
+    return launch_large<kEpiSwiglu>(p, 0, inter, s);
   return launch_cfg<CfgM, kEpiSwiglu>(p, 0, inter, s);
 }
 

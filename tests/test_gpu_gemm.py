@@ -181,6 +181,31 @@ def test_column_split_launch_sampled_rows():
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, tol, "bf16")
 
 
+@pytest.mark.parametrize("m,n,k", [(4000, 4000, 256), (4000, 4000, 384), (4096, 4096, 640)],
+                         ids=lambda v: str(v))
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_large_tiles_whole_k_tiles_sampled_rows(m, n, k, out_dtype):
+    """Shapes that fill the chip with 256x256 tiles and whose K is a whole
+    number of 128-wide K tiles run the software-pipelined one-wave-per-SIMD
+    kernel: K = 256 is its shortest case (two K tiles, re-copies from the
+    start), 384 and 640 run whole pipelines; ragged M and N tiles.  Sampled
+    rows (first and last tile rows included) against the oracle, every
+    column."""
+    say(f"gemm large pipelined {m}x{n}x{k} {out_dtype}")
+    x = rand_bf16(40 + k, m, k, outliers=2)
+    w = rand_bf16(41 + k, n, k, 0.02)
+    a = quantize_dev(x)
+    wq = quantize_dev(w)
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out = nv.gemm(a, wq, out_dtype=dt)
+    rows = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, m - 1],
+                                     np.random.default_rng(k).integers(0, m, 90)]))
+    ac, as_, ag = host_q(a)
+    wc, ws, wg = host_q(wq)
+    ref, tol = O.gemm(ac[rows], as_[rows], ag, wc, ws, wg, k)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, tol, out_dtype)
+
+
 def test_gdn_in_proj_full_size_sampled_rows():
     """32768 x 16480 x 5120 fused GDN in-projection with the gate epilogue:
     256 sampled rows (first and last row tiles included) against the
