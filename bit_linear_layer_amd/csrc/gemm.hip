@@ -350,27 +350,46 @@ __device__ __attribute__((always_inline)) inline void swiglu_epilogue(
   const bool quant = p.ep.hq_codes != nullptr;
   constexpr int kRow = staged_row_bytes<kHCols>();
   barrier_lds();  // every wave is done reading the last K tile
-  float amax = 0.0f;
+  // Two rows (r, r+1) of a lane's column at a time: one conversion rounds
+  // gate and up of a row to bf16 together, one rounds the two h values,
+  // and the amax runs on the two bf16 magnitudes as packed 16-bit
+  // integers (|h| >= 0: float order is integer order).  Rows and columns
+  // past the output are left out of the amax (partial tiles only).
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 amax2 = {0, 0};
+  auto rows = [&](auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int ml = (fm0 + i) * 32 + 4 * (lane >> 5);
+    for (int i = 0; i < C::FM; ++i) {
+      const int ml = (fm0 + i) * 32 + 4 * (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < FH; ++j) {
-      const int hl = wn * TH + j * 32 + (lane & 31);
-      const int hcol = n0 + hl;
+      for (int j = 0; j < FH; ++j) {
+        const int hl = wn * TH + j * 32 + (lane & 31);
+        const int hcol = n0 + hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mloc = ml + 8 * (r >> 2) + (r & 3);
-        const int m = m0 + mloc;
-        const float g = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j][r] * sg));
-        const float u = bf16_bits_to_f32(f32_to_bf16_bits(acc[i][j + FH][r] * su));
-        const uint32_t hb = f32_to_bf16_bits(silu(g) * u);
-        if (m < p.M && hcol < p.ep.inter) amax = fmaxf(amax, __uint_as_float((hb & 0x7FFFu) << 16));
-        *reinterpret_cast<uint16_t*>(smem + mloc * kRow + hl * 2) = (uint16_t)hb;
+        for (int r = 0; r < 16; r += 2) {
+          const int mloc = ml + 8 * (r >> 2) + (r & 3);  // rows mloc, mloc + 1
+          const uint32_t gu0 = pack_bf16x2(acc[i][j][r] * sg, acc[i][j + FH][r] * su);
+          const uint32_t gu1 = pack_bf16x2(acc[i][j][r + 1] * sg, acc[i][j + FH][r + 1] * su);
+          const float h0 = silu(__uint_as_float(gu0 << 16)) * __uint_as_float(gu0 & 0xFFFF0000u);
+          const float h1 = silu(__uint_as_float(gu1 << 16)) * __uint_as_float(gu1 & 0xFFFF0000u);
+          const uint32_t hh = pack_bf16x2(h0, h1);
+          uint32_t keep = 0x7FFF7FFFu;
+          if constexpr (!FULL) {
+            const int m = m0 + mloc;
+            keep = hcol < p.ep.inter ? (m < p.M ? 0x7FFFu : 0u) | (m + 1 < p.M ? 0x7FFF0000u : 0u) : 0u;
+          }
+          amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, hh & keep));
+          *reinterpret_cast<uint16_t*>(smem + mloc * kRow + hl * 2) = (uint16_t)hh;
+          *reinterpret_cast<uint16_t*>(smem + (mloc + 1) * kRow + hl * 2) = (uint16_t)(hh >> 16);
+        }
       }
     }
-  }
+  };
+  if (m0 + C::BM <= p.M && n0 + kHCols <= p.ep.inter) rows(std::true_type{});
+  else rows(std::false_type{});
   if (p.ep.partials != nullptr) {
+    float amax = __uint_as_float((uint32_t)(amax2[0] > amax2[1] ? amax2[0] : amax2[1]) << 16);
     amax = wave_max(amax);  // |h| >= 0: float order is unsigned integer order
     if (lane == 0)
       atomicMax(reinterpret_cast<unsigned int*>(p.ep.partials) + blockIdx.x % p.ep.n_partials,
