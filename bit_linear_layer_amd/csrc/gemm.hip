@@ -648,7 +648,7 @@ template <class C, int EPI>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
   static_assert(C::kWavesPerSimd == 1, "one wave per SIMD");
-  static_assert((C::FM + C::FN) % C::FM == 0 && C::FN % ((C::FM + C::FN) / C::FM) == 0, "decode split");
+  static_assert((C::FM + C::FN) % C::FM == 0, "decode split");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tiles_m = (p.M + C::BM - 1) / C::BM;
   constexpr int kCols = tile_cols<C, EPI>();
@@ -750,6 +750,7 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
       const bool dec = t < 7 || MORE;
       constexpr int kPerRegion = NF / C::FM;
       constexpr int kPerStep = (kPer + 3) / 4;
+      constexpr int kCopiesPerRegion = (kPerStep + C::FM - 1) / C::FM;
       half8 nxt[NF];
 #pragma unroll
       for (int r = 0; r < C::FM; ++r) {
@@ -772,8 +773,14 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
         for (int j = 0; j < C::FN; ++j)
           acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[r], cur[C::FM + j], acc[r][j], 0, 0, 0);
         if constexpr (MORE) {
-          if (t >= 4 && r < kPerStep && (t - 4) * kPerStep + r < kPer)
-            ld.issue_slot(smem + (kt % 3) * C::kStage, min(kt + 3, nk - 1), (t - 4) * kPerStep + r);
+          if (t >= 4) {
+#pragma unroll
+            for (int q = 0; q < kCopiesPerRegion; ++q) {
+              const int i = (t - 4) * kPerStep + r * kCopiesPerRegion + q;
+              if (r * kCopiesPerRegion + q < kPerStep && i < kPer)
+                ld.issue_slot(smem + (kt % 3) * C::kStage, min(kt + 3, nk - 1), i);
+            }
+          }
         }
         if (dec) {
           if constexpr (C::kSchedValu > 0) {
@@ -836,6 +843,7 @@ using CfgM = TileCfg<128, 128, 2, 2, 0>;  // medium shapes / better wave fill
 using CfgS = TileCfg<32, 128, 1, 4, 0>;   // M <= 32
 using CfgH = TileCfg<256, 128, 4, 2, 7>;  // the columns past whole waves of CfgL tiles
 using CfgP = TileCfg<256, 256, 2, 2, 4>;  // CfgL's tiles, one wave per SIMD (gemm_kernel_pipe)
+using CfgQ = TileCfg<256, 128, 4, 1, 6>;  // CfgH's tiles, one wave per SIMD (gemm_kernel_pipe)
 
 // 256x256 tiles: the pipelined one-wave-per-SIMD kernel when K is a whole
 // number (>= 2) of K tiles, else the two-wave kernel with its tail path.
@@ -843,6 +851,11 @@ template <int EPI>
 hipError_t launch_large(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   if (p.K % kBK == 0 && p.K >= 2 * kBK) return launch_cfg<CfgP, EPI, true>(p, n_lo, n_hi, s);
   return launch_cfg<CfgL, EPI>(p, n_lo, n_hi, s);
+}
+// 256x128 tiles, likewise.
+hipError_t launch_half(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
+  if (p.K % kBK == 0 && p.K >= 2 * kBK) return launch_cfg<CfgQ, kEpiPlain, true>(p, n_lo, n_hi, s);
+  return launch_cfg<CfgH, kEpiPlain>(p, n_lo, n_hi, s);
 }
 
 double fill(int64_t tiles) {
@@ -873,7 +886,7 @@ hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStr
         if (fill(tm * ((rest + 127) / 128)) < 0.9) continue;
         const hipError_t e = launch_large<kEpiPlain>(p, n_lo, n_lo + 256 * k, s);
         if (e != hipSuccess) return e;
-        return launch_cfg<CfgH, kEpiPlain>(p, n_lo + 256 * k, n_hi, s);
+        return launch_half(p, n_lo + 256 * k, n_hi, s);
       }
     }
     return launch_large<kEpiPlain>(p, n_lo, n_hi, s);

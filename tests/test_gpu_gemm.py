@@ -163,21 +163,23 @@ def test_single_global_scale_mismatch_is_detected():
     assert off_by_far >= 3  # the wide-sigma segments really differ in scale
 
 
-def test_column_split_launch_sampled_rows():
+@pytest.mark.parametrize("k", [272, 256, 384])
+def test_column_split_launch_sampled_rows(k):
     """M = 8192, N = 5120 (the MLP down projection's output): 640 tiles of
     256x256 leave a half-empty last wave, so the columns past 4096 run as
-    256x128 tiles in a second launch.  Short ragged K; 192 sampled rows
+    256x128 tiles in a second launch.  K = 272 (ragged last K tile) runs the
+    two-wave kernels, K = 256 and 384 the pipelined ones.  192 sampled rows
     against the oracle, every column, both sides of the split."""
-    say("gemm column split 8192x5120x272")
-    x = rand_bf16(31, 8192, 272)
-    w = rand_bf16(32, 5120, 272, 0.05)
+    say(f"gemm column split 8192x5120x{k}")
+    x = rand_bf16(31, 8192, k)
+    w = rand_bf16(32, 5120, k, 0.05)
     a = quantize_dev(x)
     wq = quantize_dev(w)
     out = nv.gemm(a, wq, out_dtype=torch.bfloat16)
     rows = np.unique(np.concatenate([[0, 255, 256, 8191], np.random.default_rng(3).integers(0, 8192, 188)]))
     ac, as_, ag = host_q(a)
     wc, ws, wg = host_q(wq)
-    ref, tol = O.gemm(ac[rows], as_[rows], ag, wc, ws, wg, 272)
+    ref, tol = O.gemm(ac[rows], as_[rows], ag, wc, ws, wg, k)
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, tol, "bf16")
 
 
