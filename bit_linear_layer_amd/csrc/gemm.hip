@@ -687,14 +687,23 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
   const int nk = p.K / kBK;  // >= 2, K % 128 == 0 (checked by the launcher)
   AsyncLoader<C, EPI> ld;
   ld.init(p, m0, n0, n_hi, wave, lane);
-  // Every wave keeps exactly two tiles' copies in flight behind the one it
-  // waits for: past the last tile it re-copies the last tile (in bounds)
-  // into a stage nobody reads again, so the waits are the same every tile
-  // and the K loop has no branches.
+  // A tile's copies go out in two parts: slots [0, kPart1) during k-steps
+  // 4-7 of the tile three before it (into the stage that tile has just
+  // released), slots [kPart1, kPer) during k-steps 0-3 of the tile two
+  // before it, spread one or two per region.  A wave can keep only a few
+  // LDS-DMA copies in flight: beyond that, issuing the next one stalls it
+  // (measured: issuing three whole tiles back to back took ~12K cycles, and
+  // the wait for the first then took none), so no burst is longer than a
+  // tile and a half.  Every wave keeps exactly the copies of one tile in
+  // flight behind the one it waits for: past the last tile it re-copies the
+  // last tile (in bounds) into a stage nobody reads again, so the waits are
+  // the same every tile and the K loop has no branches.
+  constexpr int kPart1 = (kPer + 1) / 2;
   ld.issue(smem, 0);
   ld.issue(smem + C::kStage, 1);
-  ld.issue(smem + 2 * C::kStage, min(2, nk - 1));
-  wait_vmem<2 * kPer>();  // tile 0 landed
+#pragma unroll
+  for (int i = 0; i < kPart1; ++i) ld.issue_slot(smem + 2 * C::kStage, min(2, nk - 1), i);
+  wait_vmem<kPer + kPart1>();  // tile 0 landed
   barrier_lds();
 
   u32x4 c_lo[NF];
@@ -743,14 +752,10 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
       // The k-step in FM regions, each scheduled as one unit: region r
       // issues the MFMAs of accumulator row r interleaved with the decode of
       // two fragments for the next k-step (W fragments first: every MFMA of
-      // the next step's first region needs all of them) and, in k-steps 4-7,
-      // one of the copies of tile kt+3 into this tile's stage.  Issued back
-      // to back, the copies stall the wave (and so its MFMAs) until the
-      // memory pipeline takes them.
+      // the next step's first region needs all of them) and its share of the
+      // copies of later tiles (at most one or two: see above).
       const bool dec = t < 7 || MORE;
       constexpr int kPerRegion = NF / C::FM;
-      constexpr int kPerStep = (kPer + 3) / 4;
-      constexpr int kCopiesPerRegion = (kPerStep + C::FM - 1) / C::FM;
       half8 nxt[NF];
 #pragma unroll
       for (int r = 0; r < C::FM; ++r) {
@@ -772,14 +777,18 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
           acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[r], cur[C::FM + j], acc[r][j], 0, 0, 0);
-        if constexpr (MORE) {
-          if (t >= 4) {
+        if (MORE || t < 4) {
+          // k-steps 4-7: part 1 of tile kt+3 into this tile's stage; k-steps
+          // 0-3: part 2 of tile kt+2 (whose part 1 went out one tile ago)
+          const int base = t < 4 ? kPart1 : 0, size = t < 4 ? kPer - kPart1 : kPart1;
+          const int per_step = (size + 3) / 4, per_region = (per_step + C::FM - 1) / C::FM;
+          const int tgt = t < 4 ? kt + 2 : kt + 3;
 #pragma unroll
-            for (int q = 0; q < kCopiesPerRegion; ++q) {
-              const int i = (t - 4) * kPerStep + r * kCopiesPerRegion + q;
-              if (r * kCopiesPerRegion + q < kPerStep && i < kPer)
-                ld.issue_slot(smem + (kt % 3) * C::kStage, min(kt + 3, nk - 1), i);
-            }
+          for (int q = 0; q < per_region; ++q) {
+            const int o = r * per_region + q;  // copy o of this k-step
+            const int i = (t & 3) * per_step + o;
+            if (o < per_step && i < size)
+              ld.issue_slot(smem + (tgt % 3) * C::kStage, min(tgt, nk - 1), base + i);
           }
         }
         if (dec) {
