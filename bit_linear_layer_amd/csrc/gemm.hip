@@ -882,24 +882,30 @@ hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStr
   if (p.M <= 32) return launch_cfg<CfgS, kEpiPlain>(p, n_lo, n_hi, s);
   const int64_t tl = (int64_t)((p.M + 255) / 256) * ((n + 255) / 256);
   const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((n + 127) / 128);
-  if (p.M >= 256 && n >= 256 && fill(tl) >= 0.8 * fill(tmd)) {
+  const bool pipe = p.K % kBK == 0 && p.K >= 2 * kBK;
+  const bool large = p.M >= 256 && n >= 256 && fill(tl) >= 0.8 * fill(tmd);
+  if (p.M >= 256 && n >= 256 && (large || pipe) && fill(tl) < 0.9) {
     // A partly filled last wave of 256x256 tiles: keep whole waves of them
-    // on the leading columns and cover the rest with 256x128 tiles, a wave
-    // of half-size work instead of a half-empty wave (two launches on the
-    // stream; every output column still sees its whole K).
-    const int64_t tm = (p.M + 255) / 256;
-    if (fill(tl) < 0.9) {
-      for (int k = n / 256 - 1; k > 0; --k) {
-        if ((tm * k) % 256 != 0) continue;
-        const int rest = n - 256 * k;
-        if (fill(tm * ((rest + 127) / 128)) < 0.9) continue;
-        const hipError_t e = launch_large<kEpiPlain>(p, n_lo, n_lo + 256 * k, s);
-        if (e != hipSuccess) return e;
-        return launch_half(p, n_lo + 256 * k, n_hi, s);
-      }
+    // on the leading columns and cover the rest in a second launch with
+    // 256x128 tiles, or with 128x128 tiles when those fill the last wave
+    // and 256x128 ones would not (a wave of smaller work instead of a
+    // half-empty wave; every output column still sees its whole K in the
+    // same order, so the outputs are bit-identical).
+    const int64_t tm = (p.M + 255) / 256, tm128 = (p.M + 127) / 128;
+    for (int k = n / 256; k > 0; --k) {
+      if ((tm * k) % 256 != 0) continue;
+      const int rest = n - 256 * k;
+      if (rest <= 0) continue;
+      const bool half = fill(tm * ((rest + 127) / 128)) >= 0.9;
+      const bool quarter = pipe && fill(tm128 * ((rest + 127) / 128)) >= 0.9;
+      if (!half && !quarter) continue;
+      const hipError_t e = launch_large<kEpiPlain>(p, n_lo, n_lo + 256 * k, s);
+      if (e != hipSuccess) return e;
+      if (half) return launch_half(p, n_lo + 256 * k, n_hi, s);
+      return launch_cfg<CfgM, kEpiPlain>(p, n_lo + 256 * k, n_hi, s);
     }
-    return launch_large<kEpiPlain>(p, n_lo, n_hi, s);
   }
+  if (large) return launch_large<kEpiPlain>(p, n_lo, n_hi, s);
   return launch_cfg<CfgM, kEpiPlain>(p, n_lo, n_hi, s);
 }
 

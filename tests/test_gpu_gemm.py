@@ -183,16 +183,17 @@ def test_column_split_launch_sampled_rows(k):
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, tol, "bf16")
 
 
-@pytest.mark.parametrize("m,n,k", [(4000, 4000, 256), (4000, 4000, 384), (4096, 4096, 640)],
+@pytest.mark.parametrize("m,n,k", [(4000, 4000, 256), (4000, 4000, 384), (4096, 4096, 640), (4096, 5120, 256)],
                          ids=lambda v: str(v))
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_large_tiles_whole_k_tiles_sampled_rows(m, n, k, out_dtype):
     """Shapes that fill the chip with 256x256 tiles and whose K is a whole
     number of 128-wide K tiles run the software-pipelined one-wave-per-SIMD
     kernel: K = 256 is its shortest case (two K tiles, re-copies from the
-    start), 384 and 640 run whole pipelines; ragged M and N tiles.  Sampled
-    rows (first and last tile rows included) against the oracle, every
-    column."""
+    start), 384 and 640 run whole pipelines; ragged M and N tiles.  4096 x
+    5120 (the act-quant GEMM's shape) runs one wave of 256x256 tiles on
+    columns 0-4095 and 128x128 tiles on the rest.  Sampled rows (first and
+    last tile rows included) against the oracle, every column."""
     say(f"gemm large pipelined {m}x{n}x{k} {out_dtype}")
     x = rand_bf16(40 + k, m, k, outliers=2)
     w = rand_bf16(41 + k, n, k, 0.02)
