@@ -12,8 +12,10 @@ Prints ONE JSON line: TFLOP/s including activation quantization (algorithmic
 2*M*N*K of both GEMMs over the time of every stage), the roofline of the
 dominant kernel (the gate|up GEMM with the SiLU*mul epilogue, timed live
 with HIP events on the launch stream), the decode-shape (M=8)
-weight-streaming GB/s, and the CPU oracle timed on a bounded sample of the
-same workload.
+weight-streaming GB/s, the other linear-layer workloads (the tiny 32x128x256
+layer's latency, the 4096x5120x5120 act-quant GEMM, the 32K-token GDN
+in-projection) under "secondary", and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -190,7 +192,8 @@ def main():
 
     # --------------------------------------------- decode shape (M = 8)
     if not args.no_secondary:
-        result["secondary"] = secondary(nv, W, torch, np, dev, stream, log)
+        result["secondary"] = small_configs(nv, W, torch, dev, stream, log)
+        result["secondary"].update(secondary(nv, W, torch, np, dev, stream, log))
         result["secondary"].update(kv_fp8(nv, W, torch, dev, stream, log))
         result["secondary"].update(mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g,
                                                 w_d, d_offs, d_g, hq, h, out, ws_x, ws_h, flops))
@@ -282,6 +285,32 @@ def kv_fp8(nv, W, torch, dev, stream, log):
         log(f"{k}: {v['us']} us = {v['GBps']} GB/s")
     return {"kv_fp8_cache": {"workload": wl.name, "algorithmic_bytes_per_element": "write 3, read 3, calibrate 2",
                              **res}}
+
+
+def small_configs(nv, W, torch, dev, stream, log):
+    """The two smaller linear-layer workloads: the tiny 32x128x256 layer
+    (fp32 output; latency of quantize X + GEMM, the weight pre-quantized)
+    and the 4096x5120x5120 activation-quantize + GEMM (bf16 output,
+    TFLOP/s including the activation quantization)."""
+    res = {}
+    for wl, key in ((W.tiny(), "tiny_m32"), (W.act_quant_gemm(), "act_quant_gemm_m4096")):
+        x = wl.x.to(dev)
+        w = nv.quantize(wl.weights[0][1].to(dev))
+        a = nv.empty_nvfp4(x.shape[0], x.shape[1], dev)
+        ws = nv.workspace_for(x.shape[0], x.shape[1], dev)
+        out = torch.empty((x.shape[0], w.rows), dtype=torch.float32 if wl.out_dtype == "f32" else torch.bfloat16,
+                          device=dev)
+
+        def step():
+            nv.nvfp4_quantize(x, a, nv.SCALE_DYNAMIC, ws)
+            nv.nvfp4_gemm(a, w, out)
+
+        ms = time_steps(torch, stream, step, steps=100, warmup=10)
+        fl = 2.0 * x.shape[0] * w.rows * x.shape[1]
+        res[key] = {"workload": wl.name, "us_quantize_plus_gemm": round(ms * 1e3, 2),
+                    "TFLOPs_incl_act_quant": round(fl / (ms * 1e-3) / 1e12, 2)}
+        log(f"{wl.name}: quantize + gemm {ms * 1e3:.1f} us = {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    return res
 
 
 def secondary(nv, W, torch, np, dev, stream, log):

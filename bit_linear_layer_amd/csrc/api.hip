@@ -75,6 +75,9 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
   }
   hipStream_t s = (hipStream_t)stream;
   float* partials = (float*)workspace;
+  if (flags == NVFP4_SCALE_DYNAMIC && rows * (cols / 16) <= kFusedQuantBlocks)
+    return hip_status(launch_quantize(x, x_dtype, rows, cols, ld_x, codes, ld_codes, scales,
+                                      ld_scales, global_scale, 2, partials, np, s));
   if (flags == NVFP4_SCALE_DYNAMIC) {
     const int st = hip_status(launch_amax(x, x_dtype, rows, cols, ld_x, partials, np, s));
     if (st != NVFP4_OK) return st;

@@ -112,11 +112,28 @@ template <int DT>
 __global__ __launch_bounds__(kElemThreads) void quantize_kernel(
     const uint8_t* __restrict__ x, int64_t ld_bytes, int64_t rows, int64_t bpr,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
-    int64_t ld_scales, float* __restrict__ gptr, int mode, const float* __restrict__ partials,
+    int64_t ld_scales, float* __restrict__ gptr, int mode, float* __restrict__ partials,
     int n_partials) {
   constexpr int kBlockBytes = DT == NVFP4_DTYPE_BF16 ? 32 : 64;
   float g;
-  if (mode == 0) {
+  if (mode == 2) {
+    // Small tensors, one workgroup: the amax pass runs here too (one launch
+    // instead of two).  The partials are left as the amax kernel would
+    // leave them (the max in slot 0, zeros after it).
+    float m = 0.0f;
+    for (BlockWalk it(rows, bpr); it.valid(); it.next()) {
+      RawBlock<DT> b;
+      b.load(x + it.r * ld_bytes + it.j * kBlockBytes);
+      float v[16];
+      b.to_float(v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+    m = block_max(m);
+    g = (float)((double)m / 2688.0);  // one correctly rounded division (53 >= 2*24+2)
+    if (threadIdx.x == 0) *gptr = g;
+    for (int i = threadIdx.x; i < n_partials; i += blockDim.x) partials[i] = i == 0 ? m : 0.0f;
+  } else if (mode == 0) {
     float m = 0.0f;
     for (int i = threadIdx.x; i < n_partials; i += blockDim.x) m = fmaxf(m, partials[i]);
     m = block_max(m);
@@ -176,15 +193,16 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
 
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
-                           float* g, int mode, const float* partials, int n_partials,
+                           float* g, int mode, float* partials, int n_partials,
                            hipStream_t s) {
   const int esz = dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
   const int64_t bpr = cols / 16;
   // enough workgroups to cover the chip several times, bounded so the
-  // per-workgroup reduction of the partials stays cheap
+  // per-workgroup reduction of the partials stays cheap; mode 2 (amax in
+  // the same kernel) runs as one workgroup
   int64_t wg = (rows * bpr + kElemThreads - 1) / kElemThreads;
   if (wg > 4096) wg = 4096;
-  if (wg < 1) wg = 1;
+  if (wg < 1 || mode == 2) wg = 1;
   if (dtype == NVFP4_DTYPE_BF16)
     quantize_kernel<NVFP4_DTYPE_BF16><<<(int)wg, kElemThreads, 0, s>>>(
         (const uint8_t*)x, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode,
