@@ -71,6 +71,9 @@ struct TileCfg {
   static constexpr int kChunks = (BM + BN) * 4;  // 16-byte code chunks per stage
   static constexpr int kChunkIters = (kChunks + kThreads - 1) / kThreads;
   static constexpr int kScaleIters = (BM + BN + kThreads - 1) / kThreads;
+  // waves per SIMD the pipelined kernel allows (two workgroups per CU when
+  // the accumulators are few enough for two waves' registers)
+  static constexpr int kPipeOcc = FM * FN <= 4 ? 2 : 1;
   static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile shape");
 };
 
@@ -645,7 +648,7 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
 // rewritten (with tile kt+3) only after that barrier, which every wave
 // reaches after its last read of the stage.
 template <class C, int EPI>
-__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kPipeOcc, C::kPipeOcc)))
 void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
   static_assert(C::kWavesPerSimd == 1, "one wave per SIMD");
   static_assert((C::FM + C::FN) % C::FM == 0, "decode split");
@@ -853,6 +856,7 @@ using CfgS = TileCfg<32, 128, 1, 4, 0>;   // M <= 32
 using CfgH = TileCfg<256, 128, 4, 2, 7>;  // the columns past whole waves of CfgL tiles
 using CfgP = TileCfg<256, 256, 2, 2, 4>;  // CfgL's tiles, one wave per SIMD (gemm_kernel_pipe)
 using CfgQ = TileCfg<256, 128, 4, 1, 6>;  // CfgH's tiles, one wave per SIMD (gemm_kernel_pipe)
+using CfgR = TileCfg<128, 128, 2, 2, 8>;  // CfgM's tiles (gemm_kernel_pipe, two workgroups per CU)
 
 // 256x256 tiles: the pipelined one-wave-per-SIMD kernel when K is a whole
 // number (>= 2) of K tiles, else the two-wave kernel with its tail path.
@@ -866,6 +870,12 @@ hipError_t launch_half(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   if (p.K % kBK == 0 && p.K >= 2 * kBK) return launch_cfg<CfgQ, kEpiPlain, true>(p, n_lo, n_hi, s);
   return launch_cfg<CfgH, kEpiPlain>(p, n_lo, n_hi, s);
 }
+// 128x128 tiles, likewise.
+template <int EPI>
+hipError_t launch_medium(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
+  if (p.K % kBK == 0 && p.K >= 2 * kBK) return launch_cfg<CfgR, EPI, true>(p, n_lo, n_hi, s);
+  return launch_cfg<CfgM, EPI>(p, n_lo, n_hi, s);
+}
 
 double fill(int64_t tiles) {
   const int64_t waves = (tiles + 255) / 256;
@@ -877,7 +887,7 @@ hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStr
   if (skinny_eligible(p)) return launch_gemm_skinny(p, n_lo, n_hi, gate, s);
   if (gate) {
     if (p.M <= 32) return launch_cfg<CfgS, kEpiGate>(p, n_lo, n_hi, s);
-    return launch_cfg<CfgM, kEpiGate>(p, n_lo, n_hi, s);
+    return launch_medium<kEpiGate>(p, n_lo, n_hi, s);
   }
   if (p.M <= 32) return launch_cfg<CfgS, kEpiPlain>(p, n_lo, n_hi, s);
   const int64_t tl = (int64_t)((p.M + 255) / 256) * ((n + 255) / 256);
@@ -902,11 +912,11 @@ hipError_t launch_range(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStr
       const hipError_t e = launch_large<kEpiPlain>(p, n_lo, n_lo + 256 * k, s);
       if (e != hipSuccess) return e;
       if (half) return launch_half(p, n_lo + 256 * k, n_hi, s);
-      return launch_cfg<CfgM, kEpiPlain>(p, n_lo + 256 * k, n_hi, s);
+      return launch_medium<kEpiPlain>(p, n_lo + 256 * k, n_hi, s);
     }
   }
   if (large) return launch_large<kEpiPlain>(p, n_lo, n_hi, s);
-  return launch_cfg<CfgM, kEpiPlain>(p, n_lo, n_hi, s);
+  return launch_medium<kEpiPlain>(p, n_lo, n_hi, s);
 }
 
 }  // namespace
@@ -963,7 +973,7 @@ hipError_t launch_gemm_swiglu(const GemmArgs& p, hipStream_t s) {
   const int64_t tmd = (int64_t)((p.M + 127) / 128) * ((inter + 63) / 64);
   if (p.M >= 256 && inter >= 128 && fill(tl) >= 0.8 * fill(tmd))
     return launch_large<kEpiSwiglu>(p, 0, inter, s);
-  return launch_cfg<CfgM, kEpiSwiglu>(p, 0, inter, s);
+  return launch_medium<kEpiSwiglu>(p, 0, inter, s);
 }
 
 }  // namespace nvfp4
