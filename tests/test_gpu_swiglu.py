@@ -76,10 +76,10 @@ def swiglu_bound(g_ref, g_tol, u_ref, u_tol):
 
 # (M, inter, K): tiny and ragged shapes run the 128-row tiles; 2000/2048 x
 # 3456 fills the chip with 256 x 128 tiles (the large configuration); K
-# values 208 and 144 leave ragged last K tiles, 256 and 640 are whole K
-# tiles (the software-pipelined large kernel).
+# values 208, 144, 320 leave ragged last K tiles, 256, 384 and 640 are whole
+# K tiles (the software-pipelined kernel, 128-row and 256-row tiles).
 SHAPES = [(5, 48, 64), (300, 272, 208), (1024, 1024, 320), (2000, 3456, 208), (2048, 3456, 144),
-          (2000, 3456, 256), (2048, 3456, 640)]
+          (2000, 3456, 256), (2048, 3456, 640), (1024, 1024, 256), (300, 272, 384)]
 
 
 @pytest.mark.parametrize("m,inter,k", SHAPES)
@@ -94,7 +94,7 @@ def test_swiglu_equals_unfused_chain(m, inter, k):
     assert_same_nvfp4(hq0, hq1)
 
 
-@pytest.mark.parametrize("m,inter,k", [(300, 272, 208), (2000, 3456, 208), (2000, 3456, 256)])
+@pytest.mark.parametrize("m,inter,k", [(300, 272, 208), (2000, 3456, 208), (2000, 3456, 256), (300, 272, 384)])
 def test_swiglu_against_oracle(m, inter, k):
     say(f"swiglu vs oracle {m}x{inter}x{k}")
     a, w, offs, sg = make_case(m, inter, k, seed=7 * m + k)
@@ -114,7 +114,7 @@ def test_swiglu_against_oracle(m, inter, k):
     assert_quant_exact(h, hq)
 
 
-@pytest.mark.parametrize("m,inter,k", [(300, 272, 208), (2048, 3456, 144)])
+@pytest.mark.parametrize("m,inter,k", [(300, 272, 208), (2048, 3456, 144), (300, 272, 384), (2000, 3456, 256)])
 @pytest.mark.parametrize("gscale", [1.0, 0.05, 40.0])
 def test_swiglu_static_quantized_output(m, inter, k, gscale):
     """h_q with a calibrated scale: gscale 1 uses h's own dynamic scale,
