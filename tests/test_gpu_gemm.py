@@ -183,7 +183,8 @@ def test_column_split_launch_sampled_rows(k):
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, tol, "bf16")
 
 
-@pytest.mark.parametrize("m,n,k", [(4000, 4000, 256), (4000, 4000, 384), (4096, 4096, 640), (4096, 5120, 256)],
+@pytest.mark.parametrize("m,n,k", [(4000, 4000, 256), (4000, 4000, 384), (4096, 4096, 640), (4096, 5120, 256),
+                                   (4001, 4000, 384), (8190, 5120, 256)],
                          ids=lambda v: str(v))
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_large_tiles_whole_k_tiles_sampled_rows(m, n, k, out_dtype):
@@ -192,8 +193,10 @@ def test_large_tiles_whole_k_tiles_sampled_rows(m, n, k, out_dtype):
     kernel: K = 256 is its shortest case (two K tiles, re-copies from the
     start), 384 and 640 run whole pipelines; ragged M and N tiles.  4096 x
     5120 (the act-quant GEMM's shape) runs one wave of 256x256 tiles on
-    columns 0-4095 and 128x128 tiles on the rest.  Sampled rows (first and
-    last tile rows included) against the oracle, every column."""
+    columns 0-4095 and 128x128 tiles on the rest; 4001 rows end in a
+    partial 32-row fragment; 8190 x 5120 runs 256x256 and 256x128 tiles,
+    both with a partial last fragment.  Sampled rows (first and last tile
+    rows included) against the oracle, every column."""
     say(f"gemm large pipelined {m}x{n}x{k} {out_dtype}")
     x = rand_bf16(40 + k, m, k, outliers=2)
     w = rand_bf16(41 + k, n, k, 0.02)
@@ -201,7 +204,7 @@ def test_large_tiles_whole_k_tiles_sampled_rows(m, n, k, out_dtype):
     wq = quantize_dev(w)
     dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
     out = nv.gemm(a, wq, out_dtype=dt)
-    rows = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, m - 1],
+    rows = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, m - 2, m - 1],
                                      np.random.default_rng(k).integers(0, m, 90)]))
     ac, as_, ag = host_q(a)
     wc, ws, wg = host_q(wq)
