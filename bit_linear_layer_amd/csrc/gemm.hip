@@ -636,17 +636,17 @@ void gemm_kernel(const GemmArgs p, int n_lo, int n_hi) {
   finish_tile<C, EPI>(p, acc, m0, n0, n_hi, fm0, fn0, wn, lane, smem);
 }
 
-// Large shapes whose K is a whole number (>= 2) of 128-wide tiles: one wave
-// per SIMD, each owning 128x128 outputs (16 accumulator fragments, held in
-// the accumulation registers), so every decoded fragment feeds four MFMAs
-// and a k-step decodes 8 fragments for 16 MFMAs.  One wave per SIMD has no
-// second wave to cover its stalls, so the K loop is software-pipelined
-// across tiles: the codes of k-steps 4-7 are read from LDS during k-step 1,
-// the next tile's k-steps 0-3 and scales during k-step 4 (after the
-// workgroup barrier that certifies that tile's copies), and k-step 7
-// decodes the next tile's first k-step.  The LDS stage of tile kt is
-// rewritten (with tile kt+3) only after that barrier, which every wave
-// reaches after its last read of the stage.
+// Shapes whose K is a whole number (>= 2) of 128-wide tiles: one wave per
+// SIMD (for 256x256 tiles each owning 128x128 outputs: 16 accumulator
+// fragments in the accumulation registers, so every decoded fragment feeds
+// four MFMAs and a k-step decodes 8 fragments for 16 MFMAs).  One wave per
+// SIMD has no second wave to cover its stalls, so the K loop is
+// software-pipelined across tiles: the codes of k-steps 4-7 are read from
+// LDS during k-step 1, the next tile's k-steps 0-3 and scales during k-step
+// 4 (after the workgroup barrier that certifies that tile's copies), and
+// k-step 7 decodes the next tile's first k-step.  The barrier of tile kt
+// also releases its LDS stage: every wave reaches it after its last read of
+// the stage, and copies into that stage (tile kt+3) go out only after it.
 template <class C, int EPI>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kPipeOcc, C::kPipeOcc)))
 void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
@@ -754,9 +754,9 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
       }
       // The k-step in FM regions, each scheduled as one unit: region r
       // issues the MFMAs of accumulator row r interleaved with the decode of
-      // two fragments for the next k-step (W fragments first: every MFMA of
-      // the next step's first region needs all of them) and its share of the
-      // copies of later tiles (at most one or two: see above).
+      // NF/FM fragments for the next k-step (W fragments first: every MFMA
+      // of the next step's first region needs all of them) and its share of
+      // the copies of later tiles (at most one or two: see above).
       const bool dec = t < 7 || MORE;
       constexpr int kPerRegion = NF / C::FM;
       half8 nxt[NF];
