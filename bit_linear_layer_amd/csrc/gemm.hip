@@ -701,12 +701,12 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
   // flight behind the one it waits for: past the last tile it re-copies the
   // last tile (in bounds) into a stage nobody reads again, so the waits are
   // the same every tile and the K loop has no branches.
+  // The prologue copies tiles 0 and 1 only; the first tile sends all of
+  // tile 2 in its k-steps 0-3.
   constexpr int kPart1 = (kPer + 1) / 2;
   ld.issue(smem, 0);
   ld.issue(smem + C::kStage, 1);
-#pragma unroll
-  for (int i = 0; i < kPart1; ++i) ld.issue_slot(smem + 2 * C::kStage, min(2, nk - 1), i);
-  wait_vmem<kPer + kPart1>();  // tile 0 landed
+  wait_vmem<kPer>();  // tile 0 landed
   barrier_lds();
 
   u32x4 c_lo[NF];
@@ -724,9 +724,11 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
     cur[f] = decode8(c_lo[f][0], s2[f]);
   }
 
-  // One K tile; MORE: a next tile follows (its first k-step is decoded here).
-  auto tile = [&](int kt, auto more_tag) __attribute__((always_inline)) {
+  // One K tile; MORE: a next tile follows (its first k-step is decoded here);
+  // FIRST: tile 0.
+  auto tile = [&](int kt, auto more_tag, auto first_tag) __attribute__((always_inline)) {
     constexpr bool MORE = decltype(more_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const uint8_t* st = smem + (kt % 3) * C::kStage;
     u32x4 c_hi[NF], n_lo[NF];
     uint32_t nsc[NF];
@@ -782,8 +784,10 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
           acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[r], cur[C::FM + j], acc[r][j], 0, 0, 0);
         if (MORE || t < 4) {
           // k-steps 4-7: part 1 of tile kt+3 into this tile's stage; k-steps
-          // 0-3: part 2 of tile kt+2 (whose part 1 went out one tile ago)
-          const int base = t < 4 ? kPart1 : 0, size = t < 4 ? kPer - kPart1 : kPart1;
+          // 0-3: part 2 of tile kt+2 (whose part 1 went out one tile ago),
+          // all of tile 2 in the first tile
+          const int base = t < 4 && !FIRST ? kPart1 : 0;
+          const int size = t < 4 ? (FIRST ? kPer : kPer - kPart1) : kPart1;
           const int per_step = (size + 3) / 4, per_region = (per_step + C::FM - 1) / C::FM;
           const int tgt = t < 4 ? kt + 2 : kt + 3;
 #pragma unroll
@@ -818,8 +822,9 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
       }
     }
   };
-  for (int kt = 0; kt + 1 < nk; ++kt) tile(kt, std::true_type{});
-  tile(nk - 1, std::false_type{});
+  tile(0, std::true_type{}, std::true_type{});
+  for (int kt = 1; kt + 1 < nk; ++kt) tile(kt, std::true_type{}, std::false_type{});
+  tile(nk - 1, std::false_type{}, std::false_type{});
   wait_vmem<0>();  // the re-copies have landed before the epilogue reuses LDS
 
   finish_tile<C, EPI>(p, acc, m0, n0, n_hi, fm0, fn0, wn, lane, smem);
