@@ -103,7 +103,10 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
  * > 448 saturates, g == 0 or an all-zero block gives 0); per element,
  * magnitude = E2M1 nearest to the exact |x| / (scale * g) (ties to even,
  * > 6 saturates, scale 0 gives 0), sign = IEEE sign bit of x.
- * Two kernel launches (amax pass, quantize pass) on `stream`.
+ * Two kernel launches (amax pass, quantize pass) on `stream`; one for
+ * DYNAMIC with at most 1024 blocks of 16 (the amax pass runs inside the
+ * one-workgroup quantize kernel and leaves the workspace as the amax pass
+ * would).
  */
 int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
                    uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
