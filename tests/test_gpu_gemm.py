@@ -212,6 +212,34 @@ def test_large_tiles_whole_k_tiles_sampled_rows(m, n, k, out_dtype):
     assert_close(out[torch.from_numpy(rows).to(DEV)], ref, tol, out_dtype)
 
 
+def padded_nvfp4(rows, cols, extra_codes, extra_scales):
+    """An NVFP4 tensor whose code and scale rows are longer than needed."""
+    codes = torch.full((rows, cols // 2 + extra_codes), 0x77, dtype=torch.uint8, device=DEV)
+    scales = torch.full((rows, cols // 16 + extra_scales), 0x7E, dtype=torch.uint8, device=DEV)
+    return nv.NVFP4Tensor(codes, scales, torch.empty(1, dtype=torch.float32, device=DEV), rows, cols)
+
+
+@pytest.mark.parametrize("m,n,k", [(4096, 4096, 384), (2048, 1024, 256)], ids=lambda v: str(v))
+def test_padded_operand_strides_pipelined(m, n, k):
+    """Operands whose code and scale rows are padded beyond K (the padding
+    holds large nonzero codes and scales that must never be read) on the
+    pipelined kernels (256x256 and 128x128 tiles)."""
+    say(f"gemm padded strides {m}x{n}x{k}")
+    x = rand_bf16(60 + k, m, k, outliers=2)
+    w = rand_bf16(61 + k, n, k, 0.02)
+    a = padded_nvfp4(m, k, 48, 24)
+    wq = padded_nvfp4(n, k, 80, 8)
+    ws = nv.workspace_for(max(m, n), k, DEV)
+    nv.nvfp4_quantize(x, a, nv.SCALE_DYNAMIC, ws)
+    nv.nvfp4_quantize(w, wq, nv.SCALE_DYNAMIC, ws)
+    out = nv.gemm(a, wq, out_dtype=torch.float32)
+    rows = np.unique(np.concatenate([[0, 255, 256, m - 1], np.random.default_rng(k).integers(0, m, 60)]))
+    ac, as_, ag = host_q(a)
+    wc, wsc, wg = host_q(wq)
+    ref, tol = O.gemm(ac[rows], as_[rows], ag, wc, wsc, wg, k)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, tol, "f32")
+
+
 def test_gdn_in_proj_full_size_sampled_rows():
     """32768 x 16480 x 5120 fused GDN in-projection with the gate epilogue:
     256 sampled rows (first and last row tiles included) against the
