@@ -68,6 +68,8 @@ struct TileCfg {
   static constexpr int kAScale = BM * kRowScaleBytes;
   static constexpr int kBScale = BN * kRowScaleBytes;
   static constexpr int kStage = kACode + kBCode + kAScale + kBScale;
+  // the pipelined kernel's stage: scales as 16 bytes per row (see AsyncLoader)
+  static constexpr int kStageWide = kACode + kBCode + (BM + BN) * 16;
   static constexpr int kChunks = (BM + BN) * 4;  // 16-byte code chunks per stage
   static constexpr int kChunkIters = (kChunks + kThreads - 1) / kThreads;
   static constexpr int kScaleIters = (BM + BN + kThreads - 1) / kThreads;
@@ -122,11 +124,18 @@ __device__ inline int w_row(const GemmArgs& p, int n0, int n_hi, int row) {
 // Waves split the groups round-robin.  Row offsets beyond M/N are clamped
 // to the last row (results of those rows are never stored).  The K tile
 // index enters as the uniform soffset, so the per-lane offsets are fixed.
-template <class C, int EPI>
+//
+// WIDE (the pipelined kernel): each scale copy moves 16 bytes per lane, one
+// row's scale bytes of this K tile and the next (8 + 8), 64 rows per copy
+// into [row][16 B]: half as many scale copies; the second 8 bytes are not
+// used (past the last row they read beyond the buffer's end, which returns
+// zeros).
+template <class C, int EPI, bool WIDE = false>
 struct AsyncLoader {
   static constexpr int kWaves = C::kThreads / 64;
+  static constexpr int kScaleRows = WIDE ? 64 : 32;  // rows per scale copy
   static constexpr int kCodeGroups = (C::BM + C::BN) / 32 * 2;
-  static constexpr int kScaleGroups = (C::BM + C::BN) / 32;
+  static constexpr int kScaleGroups = (C::BM + C::BN) / kScaleRows;
   static constexpr int kCodePer = (kCodeGroups + kWaves - 1) / kWaves;
   static constexpr int kScalePer = (kScaleGroups + kWaves - 1) / kWaves;
   i32x4 ra_c, ra_s, rw_c, rw_s;
@@ -157,12 +166,19 @@ struct AsyncLoader {
     for (int i = 0; i < kScalePer; ++i) {
       int g = wave + i * kWaves;
       if (g >= kScaleGroups) g = 0;
-      const bool isB = g >= C::BM / 32;
-      const int f = isB ? g - C::BM / 32 : g;
-      const int row = f * 32 + (lane & 31), h = lane >> 5;
-      const int grow = isB ? w_row<C, EPI>(p, n0, n_hi, row) : min(m0 + row, p.M - 1);
-      svoff[i] = (int)(grow * (isB ? p.ldw_s : p.lda_s)) + h * 4;
-      slds[i] = C::kACode + C::kBCode + (isB ? C::kAScale : 0) + f * 256;
+      const bool isB = g >= C::BM / kScaleRows;
+      const int f = isB ? g - C::BM / kScaleRows : g;
+      if constexpr (WIDE) {
+        const int row = f * 64 + lane;
+        const int grow = isB ? w_row<C, EPI>(p, n0, n_hi, row) : min(m0 + row, p.M - 1);
+        svoff[i] = (int)(grow * (isB ? p.ldw_s : p.lda_s));
+        slds[i] = C::kACode + C::kBCode + (isB ? C::BM * 16 : 0) + f * 1024;
+      } else {
+        const int row = f * 32 + (lane & 31), h = lane >> 5;
+        const int grow = isB ? w_row<C, EPI>(p, n0, n_hi, row) : min(m0 + row, p.M - 1);
+        svoff[i] = (int)(grow * (isB ? p.ldw_s : p.lda_s)) + h * 4;
+        slds[i] = C::kACode + C::kBCode + (isB ? C::kAScale : 0) + f * 256;
+      }
       sB[i] = isB;
     }
   }
@@ -180,9 +196,9 @@ struct AsyncLoader {
                                       kt * kRowCodeBytes, 0, 0);
     } else {
       const int j = i - kCodePer;
-      const bool isB = kScaleSplit ? j * kWaves >= C::BM / 32 : sB[j];
-      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[j]), 4, svoff[j],
-                                      kt * kRowScaleBytes, 0, 0);
+      const bool isB = kScaleSplit ? j * kWaves >= C::BM / kScaleRows : sB[j];
+      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[j]), WIDE ? 16 : 4,
+                                      svoff[j], kt * kRowScaleBytes, 0, 0);
     }
   }
 
@@ -190,7 +206,7 @@ struct AsyncLoader {
   // slots), slot i's operand (A or W) is the same for every wave and known
   // at compile time.
   static constexpr bool kCodeSplit = (C::BM / 32 * 2) % kWaves == 0 && kCodeGroups % kWaves == 0;
-  static constexpr bool kScaleSplit = (C::BM / 32) % kWaves == 0 && kScaleGroups % kWaves == 0;
+  static constexpr bool kScaleSplit = (C::BM / kScaleRows) % kWaves == 0 && kScaleGroups % kWaves == 0;
   __device__ __attribute__((always_inline)) void issue(uint8_t* stage, int kt) const {
 #pragma unroll
     for (int i = 0; i < kCodePer; ++i) {
@@ -200,9 +216,9 @@ struct AsyncLoader {
     }
 #pragma unroll
     for (int i = 0; i < kScalePer; ++i) {
-      const bool isB = kScaleSplit ? i * kWaves >= C::BM / 32 : sB[i];
-      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[i]), 4, svoff[i],
-                                      kt * kRowScaleBytes, 0, 0);
+      const bool isB = kScaleSplit ? i * kWaves >= C::BM / kScaleRows : sB[i];
+      llvm_amdgcn_raw_buffer_load_lds(isB ? rw_s : ra_s, (lds_u32_ptr)(stage + slds[i]), WIDE ? 16 : 4,
+                                      svoff[i], kt * kRowScaleBytes, 0, 0);
     }
   }
 };
@@ -680,15 +696,15 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
     const int off = f < C::FM ? (fm0 + f) * 2048 : C::kACode + (fn0 + f - C::FM) * 2048;
     return *reinterpret_cast<const u32x4*>(st + off + half * 1024 + lane * 16);
   };
+  // Scales: [row][16 B] (A rows, then W rows); this K tile's 8 bytes first.
   auto scale_at = [&](const uint8_t* st, int f) __attribute__((always_inline)) -> uint32_t {
-    const int off = f < C::FM ? C::kACode + C::kBCode + (fm0 + f) * 256
-                              : C::kACode + C::kBCode + C::kAScale + (fn0 + f - C::FM) * 256;
-    return *reinterpret_cast<const uint32_t*>(st + off + lane * 4);
+    const int row = (f < C::FM ? (fm0 + f) * 32 : C::BM + (fn0 + f - C::FM) * 32) + (lane & 31);
+    return *reinterpret_cast<const uint32_t*>(st + C::kACode + C::kBCode + row * 16 + (lane >> 5) * 4);
   };
 
-  constexpr int kPer = AsyncLoader<C, EPI>::kPerTile;
+  constexpr int kPer = AsyncLoader<C, EPI, true>::kPerTile;
   const int nk = p.K / kBK;  // >= 2, K % 128 == 0 (checked by the launcher)
-  AsyncLoader<C, EPI> ld;
+  AsyncLoader<C, EPI, true> ld;
   ld.init(p, m0, n0, n_hi, wave, lane);
   // A tile's copies go out in two parts: slots [0, kPart1) during k-steps
   // 4-7 of the tile three before it (into the stage that tile has just
@@ -705,7 +721,7 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
   // tile 2 in its k-steps 0-3.
   constexpr int kPart1 = (kPer + 1) / 2;
   ld.issue(smem, 0);
-  ld.issue(smem + C::kStage, 1);
+  ld.issue(smem + C::kStageWide, 1);
   wait_vmem<kPer>();  // tile 0 landed
   barrier_lds();
 
@@ -729,7 +745,7 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
   auto tile = [&](int kt, auto more_tag, auto first_tag) __attribute__((always_inline)) {
     constexpr bool MORE = decltype(more_tag)::value;
     constexpr bool FIRST = decltype(first_tag)::value;
-    const uint8_t* st = smem + (kt % 3) * C::kStage;
+    const uint8_t* st = smem + (kt % 3) * C::kStageWide;
     u32x4 c_hi[NF], n_lo[NF];
     uint32_t nsc[NF];
 #pragma unroll
@@ -746,7 +762,7 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
           // wait insertion (it cannot see inside the asm): the codes read
           // before the barrier need no further wait
           __builtin_amdgcn_s_waitcnt(0xC07F);
-          const uint8_t* nst = smem + ((kt + 1) % 3) * C::kStage;
+          const uint8_t* nst = smem + ((kt + 1) % 3) * C::kStageWide;
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
             n_lo[f] = code_at(nst, f, 0);
@@ -795,7 +811,7 @@ void gemm_kernel_pipe(const GemmArgs p, int n_lo, int n_hi) {
             const int o = r * per_region + q;  // copy o of this k-step
             const int i = (t & 3) * per_step + o;
             if (o < per_step && i < size)
-              ld.issue_slot(smem + (tgt % 3) * C::kStage, min(tgt, nk - 1), base + i);
+              ld.issue_slot(smem + (tgt % 3) * C::kStageWide, min(tgt, nk - 1), base + i);
           }
         }
         if (dec) {
@@ -838,7 +854,8 @@ hipError_t launch_cfg(const GemmArgs& p, int n_lo, int n_hi, hipStream_t s) {
   const int64_t nblocks = (int64_t)tiles_m * tiles_n;
   // three K stages; the bf16 output tile is staged in the same memory afterwards
   const size_t tile = (size_t)C::BM * staged_row_bytes<kCols>();
-  const size_t lds = 3 * (size_t)C::kStage > tile ? 3 * (size_t)C::kStage : tile;
+  const size_t stages = 3 * (size_t)(PIPE ? C::kStageWide : C::kStage);
+  const size_t lds = stages > tile ? stages : tile;
   // raising the dynamic-LDS limit is idempotent and cheap
   const void* fn;
   if constexpr (PIPE) fn = (const void*)gemm_kernel_pipe<C, EPI>;
