@@ -29,6 +29,9 @@ int check_tensor(const nvfp4_tensor* t) {
   if (t->rows >= kIndexLimit || t->cols >= kIndexLimit) return NVFP4_ERR_RANGE;
   if (t->ld_codes < t->cols / 2 || t->ld_codes % 16 != 0) return NVFP4_ERR_STRIDE;
   if (t->ld_scales < t->cols / 16 || t->ld_scales % 8 != 0) return NVFP4_ERR_STRIDE;
+  // the GEMM kernels address an operand's code and scale bytes with 32-bit
+  // offsets (and bound their buffer loads by the operand's byte size)
+  if (t->rows * t->ld_codes >= kIndexLimit || t->rows * t->ld_scales >= kIndexLimit) return NVFP4_ERR_RANGE;
   if (!aligned(t->codes, 16) || !aligned(t->scales, 8)) return NVFP4_ERR_ALIGN;
   return NVFP4_OK;
 }

@@ -113,7 +113,8 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
                    float* global_scale, int flags, void* workspace, size_t workspace_bytes,
                    void* stream);
 
-/* An NVFP4 operand of a GEMM (all pointers device). */
+/* An NVFP4 operand of a GEMM (all pointers device).  rows * ld_codes and
+ * rows * ld_scales must stay below 2^31 bytes (NVFP4_ERR_RANGE otherwise). */
 typedef struct {
   const uint8_t* codes;
   const uint8_t* scales;

@@ -82,6 +82,8 @@ def gemm(a=None, w=None, out=FAKE, dt=0, ld=8):
     (dict(a=tensor(cols=48, ldc=32)), -2), (dict(a=tensor(cols=20)), -2),
     (dict(dt=5), -3), (dict(ld=4), -4), (dict(a=tensor(ldc=24)), -4), (dict(a=tensor(lds=4)), -4),
     (dict(a=tensor(codes=FAKE + 8)), -5), (dict(out=FAKE + 1), -5),
+    # operands of 2^31 code bytes or more: beyond the kernels' 32-bit offsets
+    (dict(w=tensor(rows=1 << 20, ldc=1 << 11)), -11), (dict(a=tensor(rows=1 << 27, lds=16)), -11),
 ])
 def test_gemm_rejects_bad_arguments(kw, status):
     assert gemm(**kw) == status
