@@ -14,7 +14,8 @@ dominant kernel (the gate|up GEMM with the SiLU*mul epilogue, timed live
 with HIP events on the launch stream), the decode-shape (M=8)
 weight-streaming GB/s, the other linear-layer workloads (the tiny 32x128x256
 layer's latency, the 4096x5120x5120 act-quant GEMM, the 32K-token GDN
-in-projection) under "secondary", and the CPU oracle timed on a bounded
+in-projection) and, for context only, dense bf16 torch.matmul at the MLP
+pair's shapes under "secondary", and the CPU oracle timed on a bounded
 sample of the same workload.
 """
 from __future__ import annotations
@@ -197,6 +198,7 @@ def main():
         result["secondary"].update(kv_fp8(nv, W, torch, dev, stream, log))
         result["secondary"].update(mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g,
                                                 w_d, d_offs, d_g, hq, h, out, ws_x, ws_h, flops))
+        result["secondary"].update(bf16_context(torch, dev, stream, log, x, h, k, inter))
 
     # --------------------------------------------------- CPU oracle leg
     if not args.no_cpu_baseline:
@@ -216,6 +218,29 @@ def time_steps(torch, stream, fn, steps=10, warmup=3):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def bf16_context(torch, dev, stream, log, x, h, k, inter):
+    """Context, not a target: the same two GEMM shapes as dense bf16
+    products through torch.matmul (the vendor GEMM library), bf16 inputs of
+    the step's own X and h, N(0, 0.02) bf16 weights in [K, N] layout."""
+    gen = torch.Generator(device=dev).manual_seed(0)
+    w1 = (torch.randn((k, 2 * inter), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn((inter, k), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    o1 = torch.empty((x.shape[0], 2 * inter), dtype=torch.bfloat16, device=dev)
+    o2 = torch.empty((h.shape[0], k), dtype=torch.bfloat16, device=dev)
+    t1 = time_steps(torch, stream, lambda: torch.matmul(x, w1, out=o1))
+    t2 = time_steps(torch, stream, lambda: torch.matmul(h, w2, out=o2))
+    f1 = 2.0 * x.shape[0] * 2 * inter * k
+    f2 = 2.0 * h.shape[0] * k * inter
+    res = {"context_bf16_torch_matmul": {
+        "note": "dense bf16 GEMMs of the same shapes (vendor library), for context only",
+        "gate_up_ms": round(t1, 4), "gate_up_tflops": round(f1 / (t1 * 1e-3) / 1e12, 1),
+        "down_ms": round(t2, 4), "down_tflops": round(f2 / (t2 * 1e-3) / 1e12, 1)}}
+    log(f"context: bf16 torch.matmul gate|up {t1:.3f} ms = {f1 / (t1 * 1e-3) / 1e12:.0f} TFLOP/s, "
+        f"down {t2:.3f} ms = {f2 / (t2 * 1e-3) / 1e12:.0f} TFLOP/s")
+    del w1, w2, o1, o2
+    return res
 
 
 def mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g, w_d, d_offs, d_g, hq, h, out,
