@@ -242,8 +242,8 @@ def test_padded_operand_strides_pipelined(m, n, k):
 
 def test_gdn_in_proj_full_size_sampled_rows():
     """32768 x 16480 x 5120 fused GDN in-projection with the gate epilogue:
-    256 sampled rows (first and last row tiles included) against the
-    oracle."""
+    512 sampled rows (the first and last 256-row tiles' edges included),
+    every column (all segment boundaries), against the oracle."""
     say("fused GDN 32768x16480x5120 sampled")
     wl = W.gdn_in_proj()
     x = wl.x.to(DEV)
@@ -251,7 +251,8 @@ def test_gdn_in_proj_full_size_sampled_rows():
     a = quantize_dev(x)
     gate = dict(b_segment=4, a_segment=5, A_log=wl.extra["A_log"].to(DEV), dt_bias=wl.extra["dt_bias"].to(DEV))
     out = nv.gemm_fused_segments(a, wq, offs, seg_g, gate=gate, out_dtype=torch.bfloat16)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 32767], np.random.default_rng(2).integers(0, 32768, 251)]))
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 32511, 32512, 32767],
+                                     np.random.default_rng(2).choice(32768, 505, replace=False)]))
     ac, as_, ag = host_q(a)
     wc, ws, sg = oracle_weight(wq, offs, seg_g)
     ref, tol = O.fused_segments(ac[rows], as_[rows], ag, wc, ws, offs, sg, 5120)

@@ -56,7 +56,8 @@ def test_silu_mul_extreme_inputs():
 def test_mlp_pair_chain_sampled_rows():
     """8192-token MLP pair (gate_up [34816, 5120] two segments, SiLU*mul,
     re-quantization, down [5120, 17408]), each stage against the oracle on
-    the GPU's previous-stage output, on 128 sampled rows."""
+    the GPU's previous-stage output, on 512 sampled rows (the first and
+    last 256-row tiles' edges included)."""
     say("mlp pair 8192 chain")
     wl = W.mlp_pair()
     x = wl.x.to(DEV)
@@ -70,7 +71,8 @@ def test_mlp_pair_chain_sampled_rows():
     hq = nv.quantize(h, workspace=ws, amax_precomputed=True)
     out = nv.gemm_fused_segments(hq, wd, doffs, dg, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, 8191], np.random.default_rng(3).integers(0, 8192, 126)]))
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 7935, 7936, 8191],
+                                     np.random.default_rng(3).choice(8192, 505, replace=False)]))
     rt = torch.from_numpy(rows).to(DEV)
     # stage 1: X quantization (sampled rows, g of the whole tensor)
     assert_quant_exact(x, a, rows=rows)

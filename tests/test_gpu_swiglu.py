@@ -151,7 +151,8 @@ def test_swiglu_mlp_size_equals_unfused_and_oracle_rows():
     assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
     assert_same_nvfp4(hq0, hq1)
     inter = offs[1]
-    rows = np.unique(np.concatenate([[0, 8191], np.random.default_rng(5).integers(0, 8192, 30)]))
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 7935, 7936, 8191],
+                                     np.random.default_rng(5).integers(0, 8192, 121)]))
     ac, as_, ag = host_q(a)
     wc, wsc, g = oracle_weight(w, offs, sg)
     ref, tol = O.fused_segments(ac[rows], as_[rows], ag, wc, wsc, offs, g, 5120)
