@@ -139,14 +139,65 @@ __device__ inline float wave_max(float v) {
 // abstract, mechanism (ii): sigmoid write strength, log-space
 // softplus/exponential decay).  kind 1: sigmoid(x); kind 2:
 // -exp_alog * softplus(x + dtb) with exp_alog = exp(A_log[h]); else x.
-// One exp and one log1p: sigmoid(t) = 1/(1+e^-t), softplus(t) =
-// max(t,0) + log1p(e^-|t|).
+// Both share e = exp(-|t|): sigmoid(t) = (t >= 0 ? 1 : e) / (1 + e) and
+// softplus(t) = max(t, 0) + log1p(e).  Each piece below is within a few
+// float32 ulps (relative), all on full-rate or single transcendental
+// instructions.
+
+// exp(-a) for a >= 0.  a * log2(e) is split into its float32 rounding p and
+// the remainder d (the fma gives the rounding error exactly, plus a times
+// the constant's own tail), and 2^p from the hardware exp2 is corrected to
+// first order: 2^(p + d) = 2^p (1 + d ln 2).  For |p| <= 190 (below that the
+// result is zero) |d| < 2^-16, so the dropped second-order term is below
+// 2^-33.  Below 2^-126 the argument is lifted by 64 and the result scaled
+// back (one rounding into the subnormal range); contraction is off so that
+// the lifted argument is p + 64 exactly, not a fused a * log2(e) + 64.
+__device__ inline float exp_neg(float a) {
+#pragma clang fp contract(off)
+  const float kLog2e = 1.44269502162933349609375f;       // float32 nearest log2(e)
+  const float kLog2eTail = 1.925963033500011e-08f;       // log2(e) - kLog2e
+  const float p = -a * kLog2e;
+  const float d = fmaf(-a, kLog2e, -p) - a * kLog2eTail;
+  const bool tiny = p < -126.0f;
+  const float e0 = __builtin_amdgcn_exp2f(tiny ? p + 64.0f : p);
+  const float e = fmaf(e0, d * 0.693147180559945309f, e0);
+  return tiny ? e * 0x1p-64f : e;
+}
+
+// n / d for d in [1, 3]: hardware reciprocal, then one Newton correction of
+// the quotient (error within ~1 ulp).
+__device__ inline float div_small(float n, float d) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  const float q = n * r;
+  return fmaf(fmaf(-d, q, n), r, q);
+}
+
+// log1p(e) for e in [0, 1]: 2 atanh(s) with s = e / (2 + e) in [0, 1/3],
+// 2 s (1 + z/3 + z^2/5 + ... + z^7/15) with z = s^2 <= 1/9; the first
+// omitted term is below 2^-28 of the sum.
+__device__ inline float log1p_unit(float e) {
+  const float s = div_small(e, 2.0f + e);
+  const float z = s * s;
+  float q = 1.0f / 15.0f;
+  q = fmaf(q, z, 1.0f / 13.0f);
+  q = fmaf(q, z, 1.0f / 11.0f);
+  q = fmaf(q, z, 1.0f / 9.0f);
+  q = fmaf(q, z, 1.0f / 7.0f);
+  q = fmaf(q, z, 1.0f / 5.0f);
+  q = fmaf(q, z, 1.0f / 3.0f);
+  q = fmaf(q * z, 2.0f * s, 2.0f * s);
+  return q;
+}
+
+__device__ inline float sigmoid_from(float t, float e) { return div_small(t >= 0.0f ? 1.0f : e, 1.0f + e); }
+__device__ inline float decay_from(float t, float e, float exp_alog) {
+  return -exp_alog * (fmaxf(t, 0.0f) + log1p_unit(e));
+}
+
 __device__ inline float gate_value(float x, int kind, float exp_alog, float dtb) {
   const float t = kind == 2 ? x + dtb : x;
-  const float e = expf(-fabsf(t));
-  const float sig = (t >= 0.0f ? 1.0f : e) / (1.0f + e);
-  const float dec = -exp_alog * (fmaxf(t, 0.0f) + log1pf(e));
-  return kind == 1 ? sig : (kind == 2 ? dec : x);
+  const float e = exp_neg(fabsf(t));
+  return kind == 1 ? sigmoid_from(t, e) : (kind == 2 ? decay_from(t, e, exp_alog) : x);
 }
 
 }  // namespace dev

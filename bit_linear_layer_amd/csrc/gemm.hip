@@ -476,18 +476,29 @@ __device__ __attribute__((always_inline)) inline void finish_tile(
     }
   }
 #pragma unroll
-  for (int j = 0; j < C::FN; ++j)
+  for (int j = 0; j < C::FN; ++j) {
+    // A lane holds one column of fragment j: each gate is evaluated only in
+    // fragments where some lane's column needs it (wave-uniform branches).
+    bool any_sig = false, any_dec = false;
+    if constexpr (EPI == kEpiGate) {
+      any_sig = __ballot(kind[j] == 1) != 0;
+      any_dec = __ballot(kind[j] == 2) != 0;
+    }
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float x = acc[i][j][r] * colscale[j];
-        if constexpr (EPI == kEpiGate) {
-          acc[i][j][r] = gate_value(x, kind[j], alog[j], dtb[j]);
-        } else {
-          acc[i][j][r] = x;
+        float v = x;
+        if (any_sig || any_dec) {
+          const float t = kind[j] == 2 ? x + dtb[j] : x;
+          const float e = exp_neg(fabsf(t));
+          if (any_sig) v = kind[j] == 1 ? sigmoid_from(t, e) : v;
+          if (any_dec) v = kind[j] == 2 ? decay_from(t, e, alog[j]) : v;
         }
+        acc[i][j][r] = v;
       }
+  }
   // bf16 output through LDS: the MFMA layout gives each lane one column of
   // 16 rows, so direct stores are 2-byte scatters (one instruction per
   // element); staged, every lane stores 16 contiguous bytes.
