@@ -144,24 +144,29 @@ __device__ inline float wave_max(float v) {
 // float32 ulps (relative), all on full-rate or single transcendental
 // instructions.
 
-// exp(-a) for a >= 0.  a * log2(e) is split into its float32 rounding p and
-// the remainder d (the fma gives the rounding error exactly, plus a times
-// the constant's own tail), and 2^p from the hardware exp2 is corrected to
-// first order: 2^(p + d) = 2^p (1 + d ln 2).  For |p| <= 190 (below that the
+// exp(-a) for a >= 0, as es * 2^-64 when tiny (below 2^-126) and es
+// otherwise.  a * log2(e) is split into its float32 rounding p and the
+// remainder d (the fma gives the rounding error exactly, plus a times the
+// constant's own tail), and 2^p from the hardware exp2 is corrected to first
+// order: 2^(p + d) = 2^p (1 + d ln 2).  For |p| <= 190 (below that the
 // result is zero) |d| < 2^-16, so the dropped second-order term is below
-// 2^-33.  Below 2^-126 the argument is lifted by 64 and the result scaled
-// back (one rounding into the subnormal range); contraction is off so that
-// the lifted argument is p + 64 exactly, not a fused a * log2(e) + 64.
-__device__ inline float exp_neg(float a) {
+// 2^-33.  Tiny results are computed from the argument lifted by 64, so es
+// stays a normal number; contraction is off so that the lifted argument is
+// p + 64 exactly, not a fused a * log2(e) + 64.
+struct ExpNeg {
+  float es;
+  bool tiny;
+  __device__ float value() const { return tiny ? es * 0x1p-64f : es; }  // one rounding
+};
+__device__ inline ExpNeg exp_neg(float a) {
 #pragma clang fp contract(off)
-  const float kLog2e = 1.44269502162933349609375f;       // float32 nearest log2(e)
-  const float kLog2eTail = 1.925963033500011e-08f;       // log2(e) - kLog2e
+  const float kLog2e = 1.44269502162933349609375f;  // float32 nearest log2(e)
+  const float kLog2eTail = 1.925963033500011e-08f;  // log2(e) - kLog2e
   const float p = -a * kLog2e;
   const float d = fmaf(-a, kLog2e, -p) - a * kLog2eTail;
   const bool tiny = p < -126.0f;
   const float e0 = __builtin_amdgcn_exp2f(tiny ? p + 64.0f : p);
-  const float e = fmaf(e0, d * 0.693147180559945309f, e0);
-  return tiny ? e * 0x1p-64f : e;
+  return {fmaf(e0, d * 0.693147180559945309f, e0), tiny};
 }
 
 // n / d for d in [1, 3]: hardware reciprocal, then one Newton correction of
@@ -189,15 +194,24 @@ __device__ inline float log1p_unit(float e) {
   return q;
 }
 
-__device__ inline float sigmoid_from(float t, float e) { return div_small(t >= 0.0f ? 1.0f : e, 1.0f + e); }
-__device__ inline float decay_from(float t, float e, float exp_alog) {
-  return -exp_alog * (fmaxf(t, 0.0f) + log1p_unit(e));
+// sigmoid: for a tiny e the quotient is e itself (one rounding in value()).
+__device__ inline float sigmoid_from(float t, ExpNeg en) {
+  const float e = en.value();
+  return div_small(t >= 0.0f ? 1.0f : e, 1.0f + e);
+}
+// decay: with e below 2^-126, log1p(e) is e to float32 precision; for t < 0
+// the result -exp_alog * e is formed from the lifted es and rounded into the
+// subnormal range once (a subnormal e times exp_alog would scale its
+// rounding error by exp_alog); for t > 0 it is -exp_alog * t.
+__device__ inline float decay_from(float t, ExpNeg en, float exp_alog) {
+  if (en.tiny) return t > 0.0f ? -exp_alog * t : (-exp_alog * en.es) * 0x1p-64f;
+  return -exp_alog * (fmaxf(t, 0.0f) + log1p_unit(en.es));
 }
 
 __device__ inline float gate_value(float x, int kind, float exp_alog, float dtb) {
   const float t = kind == 2 ? x + dtb : x;
-  const float e = exp_neg(fabsf(t));
-  return kind == 1 ? sigmoid_from(t, e) : (kind == 2 ? decay_from(t, e, exp_alog) : x);
+  const ExpNeg en = exp_neg(fabsf(t));
+  return kind == 1 ? sigmoid_from(t, en) : (kind == 2 ? decay_from(t, en, exp_alog) : x);
 }
 
 }  // namespace dev

@@ -492,9 +492,9 @@ __device__ __attribute__((always_inline)) inline void finish_tile(
         float v = x;
         if (any_sig || any_dec) {
           const float t = kind[j] == 2 ? x + dtb[j] : x;
-          const float e = exp_neg(fabsf(t));
-          if (any_sig) v = kind[j] == 1 ? sigmoid_from(t, e) : v;
-          if (any_dec) v = kind[j] == 2 ? decay_from(t, e, alog[j]) : v;
+          const ExpNeg en = exp_neg(fabsf(t));
+          if (any_sig) v = kind[j] == 1 ? sigmoid_from(t, en) : v;
+          if (any_dec) v = kind[j] == 2 ? decay_from(t, en, alog[j]) : v;
         }
         acc[i][j][r] = v;
       }

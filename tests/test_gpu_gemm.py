@@ -129,6 +129,49 @@ def test_fused_segments_with_gates(out_dtype):
     assert np.all(o[:, asl] < 0) and np.all((o[:, bsl] >= 0) & (o[:, bsl] <= 1))
 
 
+@pytest.mark.parametrize("m", [200, 24, 8])  # 128-row tiles, 32-row tiles, the M <= 16 kernel
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gates_wide_argument_range(out_dtype, m):
+    """The gate epilogue far out in both tails: the b and a segments' global
+    scales are raised by powers of two (exact) until their pre-activations
+    reach about 256 in magnitude, so sigmoid saturates at 1 and underflows,
+    the decay's argument passes the float32 underflow of exp, and both gates
+    produce subnormal float32 results."""
+    say(f"gates over a wide argument range m={m} {out_dtype}")
+    wl, x, wq, offs, seg_g = small_gdn(m=m)
+    a = quantize_dev(x)
+    ac, as_, ag = host_q(a)
+    wc, ws, sg = oracle_weight(wq, offs, seg_g)
+    ref0, _ = O.fused_segments(ac, as_, ag, wc, ws, offs, sg, x.shape[1])
+    bsl, asl = slice(offs[4], offs[5]), slice(offs[5], offs[6])
+    boost = [int(np.floor(np.log2(256.0 / np.abs(ref0[:, sl]).max()))) for sl in (bsl, asl)]
+    assert min(boost) >= 0
+    seg_g2 = seg_g.clone()
+    seg_g2[4] *= 2.0 ** boost[0]
+    seg_g2[5] *= 2.0 ** boost[1]
+    gate = dict(b_segment=4, a_segment=5, A_log=wl.extra["A_log"].to(DEV), dt_bias=wl.extra["dt_bias"].to(DEV))
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out = nv.gemm_fused_segments(a, wq, offs, seg_g2, gate=gate, out_dtype=tdt)
+    wc, ws, sg2 = oracle_weight(wq, offs, seg_g2)
+    ref, tol = O.fused_segments(ac, as_, ag, wc, ws, offs, sg2, x.shape[1])
+    a_log = wl.extra["A_log"].numpy().astype(np.float64)
+    dt_bias = wl.extra["dt_bias"].numpy().astype(np.float64)
+    # the tails are really reached: sigmoid past underflow, decay arguments
+    # past the float32 underflow of exp (-103.9)
+    assert ref[:, bsl].min() < -110 and ref[:, bsl].max() > 100
+    assert (ref[:, asl] + dt_bias).min() < -110 and (ref[:, asl] + dt_bias).max() > 100
+    beta, tb, _, _ = O.gate_tolerances(ref[:, bsl], tol[:, bsl], a_log, dt_bias)
+    _, _, dec, td = O.gate_tolerances(ref[:, asl], tol[:, asl], a_log, dt_bias)
+    # float32 cannot resolve below 2^-149: a gate value in the subnormal range
+    # (or past underflow) carries a few such quanta from its last roundings
+    floor = 2.0 ** -147
+    assert_close(out[:, bsl], beta, tb + floor, out_dtype, "sigmoid gate, wide range")
+    assert_close(out[:, asl], dec, td + floor, out_dtype, "decay gate, wide range")
+    o = out.float().cpu().numpy()
+    assert np.all(o[:, asl] <= 0) and np.all((o[:, bsl] >= 0) & (o[:, bsl] <= 1))
+    assert np.all(np.isfinite(o[:, offs[4]:offs[6]]))
+
+
 def test_fused_equals_per_segment_gemms():
     say("fused == concat")
     wl, x, wq, offs, seg_g = small_gdn(m=96)
