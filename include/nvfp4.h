@@ -137,7 +137,9 @@ int nvfp4_gemm(const nvfp4_tensor* a, const nvfp4_tensor* w, void* out, int out_
 
 /* GDN gate epilogue: columns of segment b_segment become sigmoid(x); columns
  * of segment a_segment become -exp(A_log[h]) * softplus(x + dt_bias[h]),
- * h = column - start of a_segment.  x is the scaled fp32 accumulator.
+ * h = column - start of a_segment.  x is the scaled fp32 accumulator; both
+ * gates are evaluated in float32 within a few ulps of the exact function of
+ * that x (subnormal results within a few 2^-149).
  * Either segment index may be -1 (absent).  A_log and dt_bias are device
  * float32 [width of a_segment]; they may be NULL when a_segment == -1. */
 typedef struct {
