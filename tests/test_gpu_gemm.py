@@ -96,17 +96,18 @@ def test_output_canaries_and_determinism():
 # ------------------------------------------------------------ segments
 
 
-def small_gdn(m=200, scale_rows=1 / 64):
-    wl = W.gdn_in_proj(seed=0, m=m, k=512, scale_rows=scale_rows)
+def small_gdn(m=200, scale_rows=1 / 64, k=512):
+    wl = W.gdn_in_proj(seed=0, m=m, k=k, scale_rows=scale_rows)
     x = wl.x.to(DEV)
     wq, offs, seg_g = weight_segments([(n, w.to(DEV)) for n, w in wl.weights])
     return wl, x, wq, offs, seg_g
 
 
+@pytest.mark.parametrize("k", [512, 272])  # whole K tiles (pipelined kernel) and a ragged last K tile
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
-def test_fused_segments_with_gates(out_dtype):
-    say(f"fused GDN small {out_dtype}")
-    wl, x, wq, offs, seg_g = small_gdn()
+def test_fused_segments_with_gates(out_dtype, k):
+    say(f"fused GDN small {out_dtype} k={k}")
+    wl, x, wq, offs, seg_g = small_gdn(k=k)
     a = quantize_dev(x)
     gate = dict(b_segment=4, a_segment=5, A_log=wl.extra["A_log"].to(DEV), dt_bias=wl.extra["dt_bias"].to(DEV))
     tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
