@@ -22,10 +22,9 @@ hipError_t launch_amax(const void* x, int dtype, int64_t rows, int64_t cols, int
 
 // mode: 0 = dynamic (reduce partials, write *g), 1 = static (read *g),
 // 2 = dynamic in one workgroup with the amax pass in the same kernel (small
-// tensors: at most kFusedQuantBlocks 16-element blocks, kFusedQuantThreads
-// threads; writes the partials as the amax kernel would).
-constexpr int kFusedQuantThreads = 1024;
-constexpr int64_t kFusedQuantBlocks = 4 * kFusedQuantThreads;
+// tensors: at most kFusedQuantBlocks 16-element blocks; writes the partials
+// as the amax kernel would).
+constexpr int64_t kFusedQuantBlocks = 4 * kElemThreads;
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld_x,
                            uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                            float* g, int mode, float* partials, int n_partials,

@@ -22,17 +22,16 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-// Max over the workgroup (THREADS threads); every thread gets it.
-template <int THREADS>
+// Max over the workgroup (kElemThreads threads); every thread gets it.
 __device__ inline float block_max(float v) {
-  __shared__ float red[THREADS / 64];
+  __shared__ float red[kElemThreads / 64];
   v = wave_max(v);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int i = 1; i < THREADS / 64; ++i) r = fmaxf(r, red[i]);
+  for (int i = 1; i < kElemThreads / 64; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
 }
@@ -105,13 +104,12 @@ __global__ __launch_bounds__(kElemThreads) void amax_kernel(const uint8_t* __res
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
   }
-  m = block_max<kElemThreads>(m);
+  m = block_max(m);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// THREADS: kElemThreads, or kFusedQuantThreads for mode 2 (one workgroup).
-template <int DT, int THREADS>
-__global__ __launch_bounds__(THREADS) void quantize_kernel(
+template <int DT>
+__global__ __launch_bounds__(kElemThreads) void quantize_kernel(
     const uint8_t* __restrict__ x, int64_t ld_bytes, int64_t rows, int64_t bpr,
     uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
     int64_t ld_scales, float* __restrict__ gptr, int mode, float* __restrict__ partials,
@@ -131,14 +129,14 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
     }
-    m = block_max<THREADS>(m);
+    m = block_max(m);
     g = (float)((double)m / 2688.0);  // one correctly rounded division (53 >= 2*24+2)
     if (threadIdx.x == 0) *gptr = g;
     for (int i = threadIdx.x; i < n_partials; i += blockDim.x) partials[i] = i == 0 ? m : 0.0f;
   } else if (mode == 0) {
     float m = 0.0f;
     for (int i = threadIdx.x; i < n_partials; i += blockDim.x) m = fmaxf(m, partials[i]);
-    m = block_max<THREADS>(m);
+    m = block_max(m);
     g = (float)((double)m / 2688.0);  // one correctly rounded division (53 >= 2*24+2)
     if (blockIdx.x == 0 && threadIdx.x == 0) *gptr = g;
   } else {
@@ -204,22 +202,15 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
   // the same kernel) runs as one workgroup
   int64_t wg = (rows * bpr + kElemThreads - 1) / kElemThreads;
   if (wg > 4096) wg = 4096;
-  if (wg < 1) wg = 1;
-  const uint8_t* xb = (const uint8_t*)x;
-  if (mode == 2) {
-    if (dtype == NVFP4_DTYPE_BF16)
-      quantize_kernel<NVFP4_DTYPE_BF16, kFusedQuantThreads><<<1, kFusedQuantThreads, 0, s>>>(
-          xb, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode, partials, n_partials);
-    else
-      quantize_kernel<NVFP4_DTYPE_F32, kFusedQuantThreads><<<1, kFusedQuantThreads, 0, s>>>(
-          xb, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode, partials, n_partials);
-  } else if (dtype == NVFP4_DTYPE_BF16) {
-    quantize_kernel<NVFP4_DTYPE_BF16, kElemThreads><<<(int)wg, kElemThreads, 0, s>>>(
-        xb, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode, partials, n_partials);
-  } else {
-    quantize_kernel<NVFP4_DTYPE_F32, kElemThreads><<<(int)wg, kElemThreads, 0, s>>>(
-        xb, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode, partials, n_partials);
-  }
+  if (wg < 1 || mode == 2) wg = 1;
+  if (dtype == NVFP4_DTYPE_BF16)
+    quantize_kernel<NVFP4_DTYPE_BF16><<<(int)wg, kElemThreads, 0, s>>>(
+        (const uint8_t*)x, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode,
+        partials, n_partials);
+  else
+    quantize_kernel<NVFP4_DTYPE_F32><<<(int)wg, kElemThreads, 0, s>>>(
+        (const uint8_t*)x, ld_x * esz, rows, bpr, codes, ld_codes, scales, ld_scales, g, mode,
+        partials, n_partials);
   return hipGetLastError();
 }
 

@@ -104,7 +104,7 @@ size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols);
  * magnitude = E2M1 nearest to the exact |x| / (scale * g) (ties to even,
  * > 6 saturates, scale 0 gives 0), sign = IEEE sign bit of x.
  * Two kernel launches (amax pass, quantize pass) on `stream`; one for
- * DYNAMIC with at most 4096 blocks of 16 (the amax pass runs inside the
+ * DYNAMIC with at most 1024 blocks of 16 (the amax pass runs inside the
  * one-workgroup quantize kernel and leaves the workspace as the amax pass
  * would).
  */
