@@ -77,8 +77,9 @@ def read_traffic():
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards without communication along N; see the design notes)", file=sys.stderr)
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported (the layers shard "
+              "along N without communication: each GPU would run this step on its slice of every "
+              "weight segment)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
