@@ -272,14 +272,13 @@ bool skinny_eligible(const GemmArgs& p) {
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s) {
-  static int cus = 0;  // compute units of the current device (queried once)
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    cus = v > 0 ? v : 256;
-  }
+  // compute units of the current device, asked on every call (the library
+  // keeps no state between calls; the runtime answers from its own cache)
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (cus <= 0) cus = 256;
   const int quads = (p.K + 127) / 128;
   const int qpw = (quads + kWaves - 1) / kWaves;
   switch (qpw) {

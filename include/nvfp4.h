@@ -20,8 +20,9 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  Host
  *     arrays and structs are read only during the call.  The library
- *     allocates no memory; its only global state is the device's compute
- *     unit count, queried once per process to size the small-M GEMM grid.
+ *     allocates no memory and keeps no mutable state between calls, so
+ *     calls from several host threads do not interfere (calls that write
+ *     the same device memory still race, as any two kernels would).
  *   - Every call enqueues work on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and returns without synchronizing.
  *   - Matrices are row-major.  An NVFP4 matrix [rows, cols] is:

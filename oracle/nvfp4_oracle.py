@@ -434,14 +434,14 @@ def harmonize_scales(w_scales, seg_offsets, seg_g):
 # ---------------------------------------------------------------------------
 # Gated delta-rule recurrence (the GDN state update consuming beta and g)
 # ---------------------------------------------------------------------------
-# Sources: chatpaper.ai English abstract, mechanism (iii) (the delta-rule
-# recurrence holds injected noise at a plateau and forgets a state impulse
-# because each write overwrites the state along the current key direction)
-# and mechanism (ii) (write strength through a sigmoid, decay through a
-# log-space softplus/exponential); evolve.pub review, "Key claims under
-# review", third claim and "Strengths" (relS plateau, impulse erasure).  The
-# pages name Gated DeltaNet but do not write its update; this is the
-# published gated delta rule, per value head h with state S in R^{dv x dk}:
+# Sources: chatpaper.ai English abstract, mechanism (iii) (state errors
+# stay bounded and a perturbation of the state fades, since every write
+# replaces what the state held along the incoming key) and mechanism (ii)
+# (sigmoid write strength, log-space softplus/exponential decay); evolve.pub
+# review, "Key claims under review", third claim and "Strengths" (relS
+# plateau, impulse erasure).  The pages name Gated DeltaNet without writing
+# out its update; the update used here is the published gated delta rule,
+# per value head h with state S in R^{dv x dk}:
 #
 #     S_t = exp(g_t) * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
 #     o_t = S_t q_t
@@ -450,8 +450,10 @@ def harmonize_scales(w_scales, seg_offsets, seg_g):
 # (the gate epilogue's outputs, a log-space decay <= 0).  Readings: q and k
 # heads are shared by groups of value heads (value head h reads q/k head
 # h // (Hv / Hk)); with normalize=True q and k are L2-normalized over the
-# head dimension first and q is scaled by dk^-1/2 (the short convolution
-# that precedes them in a GDN layer is outside this path).
+# head dimension first and q is scaled by dk^-1/2, the query scale of the
+# published layer (a convention of that layer, not a number the pages give;
+# the short convolution that precedes q and k in a GDN layer is outside
+# this path).
 
 def l2_normalize(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)

@@ -145,3 +145,59 @@ def test_planted_mistakes_fail_the_partial_write_pin(mistake):
     b, a = 0.37, np.exp(-0.2)
     s = mistake(s0, kk, v, b, a)
     assert not np.allclose(s @ kk, (1 - b) * a * s0 @ kk + b * v, atol=1e-9)
+
+
+def test_normalized_query_reads_stored_value_scaled_by_inverse_sqrt_dk():
+    """Closed form of the normalized read.  Orthonormal keys written with
+    beta = 1 and no decay store v exactly along each key; a query c * k_j
+    with any c != 0 normalizes to sign(c) k_j and is scaled by dk^-1/2, so
+    the read is sign(c) v_j / sqrt(dk) at the head width of the GPU path
+    (128), and a query along a key not yet written reads zero.  Dropping the
+    query scale, normalizing over another axis, or leaving q unnormalized
+    all fail."""
+    rng = np.random.default_rng(9)
+    d, n, hk, hv = 128, 5, 2, 4
+    rep = hv // hk
+    basis = np.linalg.qr(rnd(rng, d, d))[0].T           # rows: orthonormal keys
+    key = lambda kh, j: basis[n * kh + j]               # slot j of key head kh
+    T = 2 * n
+    k, q = np.zeros((T, hk, d)), np.zeros((T, hk, d))
+    v = rnd(rng, T, hv, d)
+    beta = np.zeros((T, hv))
+    coef = np.zeros((T, hk))
+    slot = np.zeros((T, hk), dtype=int)
+    for t in range(T):
+        for kh in range(hk):
+            if t < n:   # token t writes slot t of every key head, key scaled arbitrarily
+                k[t, kh] = key(kh, t) * (0.01 + 3.0 * t)
+                beta[t, kh * rep:(kh + 1) * rep] = 1.0
+            else:       # no writes (beta = 0) along a spare key
+                k[t, kh] = basis[2 * n + kh]
+            slot[t, kh] = (t + 3 * kh) % n
+            coef[t, kh] = (-1) ** (t + kh) * (0.2 + 7.0 * rng.random())
+            q[t, kh] = coef[t, kh] * key(kh, slot[t, kh])
+    o, _ = O.gdn_recurrence(q, k, v, beta, np.zeros((T, hv)), normalize=True)
+    checked = 0
+    for t in range(T):
+        for h in range(hv):
+            kh = h // rep
+            j = slot[t, kh]
+            expect = np.sign(coef[t, kh]) * v[j, h] / np.sqrt(128.0) if j <= t else np.zeros(d)
+            assert np.allclose(o[t, h], expect, rtol=1e-10, atol=1e-12)
+            checked += j > t
+    assert checked > 0   # some queries read slots not yet written
+
+
+def test_query_scale_alone_leaves_normalized_output_unchanged():
+    """Scaling q alone (k fixed) by any positive factor changes nothing with
+    normalize=True; without normalization the output scales with q."""
+    rng = np.random.default_rng(10)
+    T, d = 6, 16
+    q, k, v = rnd(rng, T, 1, d), rnd(rng, T, 1, d), rnd(rng, T, 2, d)
+    beta, g = np.full((T, 2), 0.7), np.full((T, 2), -0.1)
+    o1, _ = O.gdn_recurrence(q, k, v, beta, g)
+    o2, _ = O.gdn_recurrence(q * 41.0, k, v, beta, g)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    o3, _ = O.gdn_recurrence(q, k, v, beta, g, normalize=False)
+    o4, _ = O.gdn_recurrence(q * 41.0, k, v, beta, g, normalize=False)
+    assert np.allclose(o4, 41.0 * o3, rtol=1e-12)
