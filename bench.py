@@ -47,6 +47,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode / GDN measurements")
+    ap.add_argument("--parts", default="all",
+                    help="comma list of secondary measurements to run (small, decode, gdn_in_proj, gdn, kv, "
+                         "variants, context) or 'all'; for profiling runs")
     ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration) and exit")
@@ -194,12 +197,25 @@ def main():
 
     # --------------------------------------------- decode shape (M = 8)
     if not args.no_secondary:
-        result["secondary"] = small_configs(nv, W, torch, dev, stream, log)
-        result["secondary"].update(secondary(nv, W, torch, np, dev, stream, log))
-        result["secondary"].update(kv_fp8(nv, W, torch, dev, stream, log))
-        result["secondary"].update(mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g,
-                                                w_d, d_offs, d_g, hq, h, out, ws_x, ws_h, flops))
-        result["secondary"].update(bf16_context(torch, dev, stream, log, x, h, k, inter))
+        parts = PARTS if args.parts == "all" else set(args.parts.split(","))
+        if parts - PARTS:
+            sys.exit(f"bench.py: unknown parts {sorted(parts - PARTS)}")
+        sec = result["secondary"] = {}
+        if "small" in parts:
+            sec.update(small_configs(nv, W, torch, dev, stream, log))
+        if "decode" in parts:
+            sec.update(decode(nv, W, torch, dev, stream, log))
+        if "gdn_in_proj" in parts:
+            sec.update(gdn_in_proj(nv, W, torch, dev, stream, log))
+        if "gdn" in parts:
+            sec["gdn_recurrence"] = gdn_study(nv, W, torch, stream, log, dev)
+        if "kv" in parts:
+            sec.update(kv_fp8(nv, W, torch, dev, stream, log))
+        if "variants" in parts:
+            sec.update(mlp_variants(nv, torch, dev, stream, log, x, a, w_gu, gu_offs, gu_g,
+                                    w_d, d_offs, d_g, hq, h, out, ws_x, ws_h, flops))
+        if "context" in parts:
+            sec.update(bf16_context(torch, dev, stream, log, x, h, k, inter))
 
     # --------------------------------------------------- CPU oracle leg
     if not args.no_cpu_baseline:
@@ -339,10 +355,12 @@ def small_configs(nv, W, torch, dev, stream, log):
     return res
 
 
-def secondary(nv, W, torch, np, dev, stream, log):
+PARTS = {"small", "decode", "gdn_in_proj", "gdn", "kv", "variants", "context"}
+
+
+def decode(nv, W, torch, dev, stream, log):
     """Decode-shape weight streaming (M=8 x [34816, 5120], four rotating
-    weight copies so reads come from HBM, not the 256 MB MALL) and the
-    32768-token fused GDN in-projection with gates."""
+    weight copies so reads come from HBM, not the 256 MB MALL)."""
     res = {}
     log("decode M=8 x 34816x5120: four rotating NVFP4 weight copies")
     dw = W.decode()
@@ -390,12 +408,20 @@ def secondary(nv, W, torch, np, dev, stream, log):
                         "algorithmic_bytes": alg_bytes, "quantize_plus_gemm_us": round(t_full * 1e6, 2)}
     log(f"decode: gemm {t_gemm * 1e6:.1f} us = {alg_bytes / t_gemm / 1e9:.0f} GB/s")
     del copies, base, outd
+    return res
 
+
+def gdn_in_proj(nv, W, torch, dev, stream, log):
+    """The 32768-token fused GDN in-projection with gates (six segments),
+    and the scale-harmonization study on it."""
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log("fused GDN in-projection 32768 x 16480 x 5120 with gates")
     gw = W.gdn_in_proj()
     xg = gw.x.to(dev)
     segs = [w for _, w in gw.weights]
     rows = sum(w.shape[0] for w in segs)
+    kk = segs[0].shape[1]
     wq = nv.empty_nvfp4(rows, kk, dev)
     sg = torch.empty(len(segs), dtype=torch.float32, device=dev)
     offs = [0]
@@ -429,7 +455,6 @@ def secondary(nv, W, torch, np, dev, stream, log):
     log(f"gdn in-proj: {t * 1e3:.3f} ms = {fl / t / 1e12:.0f} TFLOP/s")
     res["scale_harmonization_gdn_in_proj"] = harmonization_study(nv, torch, stream, log, gw, ag, wq, offs, sg, gate)
     del outg
-    res["gdn_recurrence"] = gdn_study(nv, W, torch, stream, log, dev)
     return res
 
 
