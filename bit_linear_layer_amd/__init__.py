@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "NVFP4Error", "NVFP4Tensor", "load", "lib_path",
-    "nvfp4_quantize", "nvfp4_quantize_workspace_bytes", "nvfp4_gemm",
+    "nvfp4_quantize", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize_noalloc", "nvfp4_gemm",
     "nvfp4_gemm_fused_segments", "nvfp4_silu_mul", "nvfp4_status_string", "nvfp4_version",
     "empty_nvfp4", "quantize", "gemm", "gemm_fused_segments", "silu_mul", "workspace_for",
     "DTYPE_BF16", "DTYPE_F32", "SCALE_DYNAMIC", "SCALE_STATIC", "AMAX_PRECOMPUTED", "MAX_SEGMENTS",
@@ -70,6 +70,9 @@ def load() -> ctypes.CDLL:
         lib.nvfp4_quantize.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P,
                                        ctypes.c_int, _P, ctypes.c_size_t, _P]
         lib.nvfp4_quantize.restype = ctypes.c_int
+        lib.nvfp4_quantize_noalloc.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _P, _I64, _P, _I64, _P,
+                                               ctypes.c_int, _P]
+        lib.nvfp4_quantize_noalloc.restype = ctypes.c_int
         lib.nvfp4_gemm.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), _P,
                                    ctypes.c_int, _I64, _P]
         lib.nvfp4_gemm.restype = ctypes.c_int
@@ -189,6 +192,18 @@ def nvfp4_quantize(x: torch.Tensor, q: NVFP4Tensor, flags: int = SCALE_DYNAMIC,
         q.codes.data_ptr(), q.codes.stride(0), q.scales.data_ptr(), q.scales.stride(0),
         q.global_scale.data_ptr(), flags, _ptr(workspace), ws_bytes, _stream(x.device, stream))
     _check(st, "nvfp4_quantize")
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, q: NVFP4Tensor, flags: int = SCALE_DYNAMIC, stream=None) -> None:
+    """C ``nvfp4_quantize_noalloc``: ``nvfp4_quantize`` without a workspace
+    (the library's static per-GPU scratch holds the amax partials)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise NVFP4Error("x must be a 2-D tensor with contiguous rows")
+    st = load().nvfp4_quantize_noalloc(
+        x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
+        q.codes.data_ptr(), q.codes.stride(0), q.scales.data_ptr(), q.scales.stride(0),
+        q.global_scale.data_ptr(), flags, _stream(x.device, stream))
+    _check(st, "nvfp4_quantize_noalloc")
 
 
 def nvfp4_gemm(a: NVFP4Tensor, w: NVFP4Tensor, out: torch.Tensor, stream=None) -> None:

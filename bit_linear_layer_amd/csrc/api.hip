@@ -46,17 +46,11 @@ int check_out(const void* out, int out_dtype, int64_t ld_out, int64_t n) {
 
 }  // namespace
 
-extern "C" {
+namespace nvfp4 {
 
-size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
-  if (rows <= 0 || cols < 16) return sizeof(float);
-  return sizeof(float) * (size_t)partial_count(rows, cols, 16);
-}
-
-int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
-                   uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
-                   float* global_scale, int flags, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+int quantize_check(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, const uint8_t* codes,
+                   int64_t ld_codes, const uint8_t* scales, int64_t ld_scales, const float* global_scale,
+                   int flags) {
   if (x == nullptr || codes == nullptr || scales == nullptr || global_scale == nullptr)
     return NVFP4_ERR_NULL;
   if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
@@ -69,15 +63,14 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
   if (ld_codes < cols / 2 || ld_codes % 8 != 0) return NVFP4_ERR_STRIDE;
   if (ld_scales < cols / 16) return NVFP4_ERR_STRIDE;
   if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(global_scale, 4)) return NVFP4_ERR_ALIGN;
-  const bool dynamic = flags != NVFP4_SCALE_STATIC;
-  const int np = partial_count(rows, cols, 16);
-  if (dynamic) {
-    if (workspace == nullptr) return NVFP4_ERR_WORKSPACE;
-    if (workspace_bytes < sizeof(float) * (size_t)np) return NVFP4_ERR_WORKSPACE;
-    if (!aligned(workspace, 4)) return NVFP4_ERR_ALIGN;
-  }
+  return NVFP4_OK;
+}
+
+int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                    int64_t ld_codes, uint8_t* scales, int64_t ld_scales, float* global_scale, int flags,
+                    float* partials, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  float* partials = (float*)workspace;
+  const int np = partial_count(rows, cols, 16);
   if (flags == NVFP4_SCALE_DYNAMIC && rows * (cols / 16) <= kFusedQuantBlocks)
     return hip_status(launch_quantize(x, x_dtype, rows, cols, ld_x, codes, ld_codes, scales,
                                       ld_scales, global_scale, 2, partials, np, s));
@@ -86,7 +79,35 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
     if (st != NVFP4_OK) return st;
   }
   return hip_status(launch_quantize(x, x_dtype, rows, cols, ld_x, codes, ld_codes, scales,
-                                    ld_scales, global_scale, dynamic ? 0 : 1, partials, np, s));
+                                    ld_scales, global_scale, flags == NVFP4_SCALE_STATIC ? 1 : 0,
+                                    partials, np, s));
+}
+
+int status_from_hip(hipError_t e) { return hip_status(e); }
+
+}  // namespace nvfp4
+
+extern "C" {
+
+size_t nvfp4_quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols < 16) return sizeof(float);
+  return sizeof(float) * (size_t)partial_count(rows, cols, 16);
+}
+
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                   uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                   float* global_scale, int flags, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  const int st = quantize_check(x, x_dtype, rows, cols, ld_x, codes, ld_codes, scales, ld_scales,
+                                global_scale, flags);
+  if (st != NVFP4_OK) return st;
+  if (flags != NVFP4_SCALE_STATIC) {
+    if (workspace == nullptr) return NVFP4_ERR_WORKSPACE;
+    if (workspace_bytes < nvfp4_quantize_workspace_bytes(rows, cols)) return NVFP4_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return NVFP4_ERR_ALIGN;
+  }
+  return quantize_launch(x, x_dtype, rows, cols, ld_x, codes, ld_codes, scales, ld_scales, global_scale,
+                         flags, (float*)workspace, stream);
 }
 
 int nvfp4_gemm_fused_segments(const nvfp4_tensor* a, const nvfp4_tensor* w, int n_segments,

@@ -30,6 +30,18 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
                            float* g, int mode, float* partials, int n_partials,
                            hipStream_t s);
 
+// nvfp4_quantize in two halves (api.hip): every argument check except the
+// workspace's, then the launches with the amax partials at `partials`
+// (unused for NVFP4_SCALE_STATIC).  nvfp4_quantize_noalloc shares both.
+int quantize_check(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, const uint8_t* codes,
+                   int64_t ld_codes, const uint8_t* scales, int64_t ld_scales, const float* global_scale,
+                   int flags);
+int quantize_launch(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                    int64_t ld_codes, uint8_t* scales, int64_t ld_scales, float* global_scale, int flags,
+                    float* partials, void* stream);
+// NVFP4_ERR_HIP for a failed HIP call (its text kept for nvfp4_status_string).
+int status_from_hip(hipError_t e);
+
 hipError_t launch_silu_mul(const uint16_t* gu, int64_t rows, int64_t inter, int64_t ld_gu,
                            uint16_t* h, int64_t ld_h, float* partials, int n_partials,
                            hipStream_t s);

@@ -20,9 +20,11 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  Host
  *     arrays and structs are read only during the call.  The library
- *     allocates no memory and keeps no mutable state between calls, so
- *     calls from several host threads do not interfere (calls that write
- *     the same device memory still race, as any two kernels would).
+ *     allocates no memory and keeps no mutable state between calls apart
+ *     from one address per device that nvfp4_quantize_noalloc looks up
+ *     once (atomically), so calls from several host threads do not
+ *     interfere (calls that write the same device memory still race, as any
+ *     two kernels would).
  *   - Every call enqueues work on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and returns without synchronizing.
  *   - Matrices are row-major.  An NVFP4 matrix [rows, cols] is:
@@ -113,6 +115,30 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int64
                    uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                    float* global_scale, int flags, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * nvfp4_quantize_noalloc -- nvfp4_quantize for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments and the same result
+ * bit for bit, without the workspace.  The amax partials of the dynamic
+ * global scale go to a static device array of NVFP4_NOALLOC_SCRATCH_BYTES
+ * held by the library on each GPU it runs on until the process ends; that
+ * covers every shape nvfp4_quantize accepts (a shape needing more would be
+ * rejected with NVFP4_ERR_WORKSPACE).  No call allocates memory.
+ *
+ *   flags    NVFP4_SCALE_DYNAMIC or NVFP4_SCALE_STATIC;
+ *            NVFP4_AMAX_PRECOMPUTED is rejected (NVFP4_ERR_FLAGS): there is
+ *            no caller workspace to hold precomputed partials.
+ * The first call on a device looks up the array's device address (one
+ * hipGetSymbolAddress, kept per device).  All calls on one GPU share the
+ * array: two dynamic calls that overlap on one GPU (different streams, or
+ * different host threads without ordering) race on it and may produce a
+ * wrong global scale.  Calls in one stream are ordered and safe.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES 4096
+int nvfp4_quantize_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                           uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                           float* global_scale, int flags, void* stream);
 
 /* An NVFP4 operand of a GEMM (all pointers device).  rows * ld_codes and
  * rows * ld_scales must stay below 2^31 bytes (NVFP4_ERR_RANGE otherwise). */

@@ -175,3 +175,22 @@ def test_harmonize_rejects_bad_arguments():
     assert call(ld=1) == -4
     assert call(g=FAKE + 2) == -5
     assert call(n=0, offs=(0,)) == -6 and call(offs=(0, 4, 7)) == -6 and call(offs=(0, 9, 8)) == -6
+
+
+def qn(**kw):
+    args = dict(x=FAKE, dt=0, rows=4, cols=32, ldx=32, codes=FAKE, ldc=16, scales=FAKE, lds=8,
+                g=FAKE, flags=0, stream=None)
+    args.update(kw)
+    return nv.load().nvfp4_quantize_noalloc(args["x"], args["dt"], args["rows"], args["cols"], args["ldx"],
+                                            args["codes"], args["ldc"], args["scales"], args["lds"], args["g"],
+                                            args["flags"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), -1), (dict(g=None), -1), (dict(dt=7), -3), (dict(flags=9), -9), (dict(flags=2), -9),
+    (dict(cols=24, ldx=24), -2), (dict(rows=0), -2), (dict(ldx=16), -4), (dict(x=FAKE + 2), -5),
+    (dict(rows=1 << 31), -11),
+])
+def test_quantize_noalloc_rejects_bad_arguments(kw, status):
+    assert qn(**kw) == status
+
