@@ -19,6 +19,8 @@ __all__ = [
     "NVFP4Error", "NVFP4Tensor", "load", "lib_path",
     "nvfp4_quantize", "nvfp4_quantize_workspace_bytes", "nvfp4_quantize_noalloc", "nvfp4_gemm",
     "nvfp4_gemm_fused_segments", "nvfp4_silu_mul", "nvfp4_status_string", "nvfp4_version",
+    "DecodeWeight", "nvfp4_decode_weight_bytes", "nvfp4_decode_weight_pack", "nvfp4_gemm_decode",
+    "nvfp4_linear_decode", "pack_decode", "gemm_decode", "linear_decode",
     "empty_nvfp4", "quantize", "gemm", "gemm_fused_segments", "silu_mul", "workspace_for",
     "DTYPE_BF16", "DTYPE_F32", "SCALE_DYNAMIC", "SCALE_STATIC", "AMAX_PRECOMPUTED", "MAX_SEGMENTS",
 ]
@@ -44,6 +46,10 @@ class _Tensor(ctypes.Structure):
 class _Gate(ctypes.Structure):
     _fields_ = [("b_segment", ctypes.c_int), ("a_segment", ctypes.c_int),
                 ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
+class _DecodeWeight(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
 class _GdnInputs(ctypes.Structure):
@@ -80,6 +86,18 @@ def load() -> ctypes.CDLL:
             ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), ctypes.c_int,
             ctypes.POINTER(ctypes.c_int64), _P, ctypes.POINTER(_Gate), _P, ctypes.c_int, _I64, _P]
         lib.nvfp4_gemm_fused_segments.restype = ctypes.c_int
+        lib.nvfp4_decode_weight_bytes.argtypes = [_I64, _I64]
+        lib.nvfp4_decode_weight_bytes.restype = ctypes.c_size_t
+        lib.nvfp4_decode_weight_pack.argtypes = [ctypes.POINTER(_Tensor), _P, ctypes.c_size_t, _P]
+        lib.nvfp4_decode_weight_pack.restype = ctypes.c_int
+        lib.nvfp4_gemm_decode.argtypes = [
+            ctypes.POINTER(_Tensor), ctypes.POINTER(_DecodeWeight), ctypes.c_int,
+            ctypes.POINTER(ctypes.c_int64), _P, ctypes.POINTER(_Gate), _P, ctypes.c_int, _I64, _P]
+        lib.nvfp4_gemm_decode.restype = ctypes.c_int
+        lib.nvfp4_linear_decode.argtypes = [
+            _P, ctypes.c_int, _I64, _I64, _P, ctypes.POINTER(_DecodeWeight), ctypes.c_int,
+            ctypes.POINTER(ctypes.c_int64), _P, ctypes.POINTER(_Gate), _P, ctypes.c_int, _I64, _P]
+        lib.nvfp4_linear_decode.restype = ctypes.c_int
         lib.nvfp4_silu_mul.argtypes = [_P, _I64, _I64, _I64, _P, _I64, _P, ctypes.c_size_t, _P]
         lib.nvfp4_silu_mul.restype = ctypes.c_int
         lib.nvfp4_gemm_swiglu.argtypes = [ctypes.POINTER(_Tensor), ctypes.POINTER(_Tensor), _P, _P, _I64,
@@ -142,6 +160,28 @@ def _round_up(v: int, a: int) -> int:
     return (v + a - 1) // a * a
 
 
+def _check_dense(t: torch.Tensor, rows: int, cols: int, device, what: str) -> None:
+    """A caller-supplied dense output or input: [rows, cols], contiguous rows
+    (any row stride), on the operands' device."""
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise NVFP4Error(f"{what} must have shape ({rows}, {cols}), got {tuple(t.shape)}")
+    if t.stride(1) != 1 or (rows > 1 and t.stride(0) < cols):
+        raise NVFP4Error(f"{what} must have contiguous rows")
+    if not t.is_cuda or t.device != torch.device(device):
+        raise NVFP4Error(f"{what} must live on {device}, got {t.device}")
+
+
+def _check_nvfp4(q: "NVFP4Tensor", rows: int, cols: int, device, what: str) -> None:
+    """An NVFP4 operand or output of [rows, cols] with room for its codes and scales."""
+    if q.rows != rows or q.cols != cols:
+        raise NVFP4Error(f"{what} is [{q.rows}, {q.cols}], expected [{rows}, {cols}]")
+    for name, t, need in (("codes", q.codes, cols // 2), ("scales", q.scales, cols // 16)):
+        if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < need or t.stride(1) != 1 or t.dtype != torch.uint8:
+            raise NVFP4Error(f"{what}.{name} must be uint8 [>= {rows}, >= {need}] with contiguous rows")
+        if not t.is_cuda or t.device != torch.device(device):
+            raise NVFP4Error(f"{what}.{name} must live on {device}, got {t.device}")
+
+
 @dataclass
 class NVFP4Tensor:
     """An NVFP4 matrix [rows, cols] in device memory: codes uint8
@@ -186,6 +226,7 @@ def nvfp4_quantize(x: torch.Tensor, q: NVFP4Tensor, flags: int = SCALE_DYNAMIC,
     strided) into the preallocated ``q``."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise NVFP4Error("x must be a 2-D tensor with contiguous rows")
+    _check_nvfp4(q, x.shape[0], x.shape[1], x.device, "q")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().nvfp4_quantize(
         x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
@@ -199,6 +240,7 @@ def nvfp4_quantize_noalloc(x: torch.Tensor, q: NVFP4Tensor, flags: int = SCALE_D
     (the library's static per-GPU scratch holds the amax partials)."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise NVFP4Error("x must be a 2-D tensor with contiguous rows")
+    _check_nvfp4(q, x.shape[0], x.shape[1], x.device, "q")
     st = load().nvfp4_quantize_noalloc(
         x.data_ptr(), _dtype_code(x), x.shape[0], x.shape[1], x.stride(0),
         q.codes.data_ptr(), q.codes.stride(0), q.scales.data_ptr(), q.scales.stride(0),
@@ -208,6 +250,7 @@ def nvfp4_quantize_noalloc(x: torch.Tensor, q: NVFP4Tensor, flags: int = SCALE_D
 
 def nvfp4_gemm(a: NVFP4Tensor, w: NVFP4Tensor, out: torch.Tensor, stream=None) -> None:
     """C ``nvfp4_gemm``: out[M, N] = A W^T with both global scales."""
+    _check_dense(out, a.rows, w.rows, a.codes.device, "out")
     da, dw = a.descriptor(), w.descriptor()
     st = load().nvfp4_gemm(ctypes.byref(da), ctypes.byref(dw), out.data_ptr(), _dtype_code(out),
                            out.stride(0), _stream(out.device, stream))
@@ -219,11 +262,9 @@ def nvfp4_gemm_fused_segments(a: NVFP4Tensor, w: NVFP4Tensor, seg_offsets, seg_g
     """C ``nvfp4_gemm_fused_segments``.  seg_offsets: host ints [n+1];
     seg_global_scales: device float32 [n]; gate: None or dict(b_segment,
     a_segment, A_log, dt_bias) with device float32 tensors."""
+    _check_dense(out, a.rows, w.rows, a.codes.device, "out")
     offs = (ctypes.c_int64 * len(seg_offsets))(*[int(o) for o in seg_offsets])
-    g = None
-    if gate is not None:
-        g = _Gate(int(gate.get("b_segment", -1)), int(gate.get("a_segment", -1)),
-                  _ptr(gate.get("A_log")), _ptr(gate.get("dt_bias")))
+    g = _gate(gate)
     da, dw = a.descriptor(), w.descriptor()
     st = load().nvfp4_gemm_fused_segments(
         ctypes.byref(da), ctypes.byref(dw), len(seg_offsets) - 1, offs, seg_global_scales.data_ptr(),
@@ -232,9 +273,75 @@ def nvfp4_gemm_fused_segments(a: NVFP4Tensor, w: NVFP4Tensor, seg_offsets, seg_g
     _check(st, "nvfp4_gemm_fused_segments")
 
 
+def _gate(gate: dict | None):
+    if gate is None:
+        return None
+    return _Gate(int(gate.get("b_segment", -1)), int(gate.get("a_segment", -1)),
+                 _ptr(gate.get("A_log")), _ptr(gate.get("dt_bias")))
+
+
+@dataclass
+class DecodeWeight:
+    """A weight [rows, cols] in the decode layout (``nvfp4_decode_weight_pack``):
+    ``data`` is a uint8 device tensor of ``nvfp4_decode_weight_bytes`` bytes."""
+    data: torch.Tensor
+    rows: int
+    cols: int
+
+    def descriptor(self) -> _DecodeWeight:
+        return _DecodeWeight(self.data.data_ptr(), self.rows, self.cols)
+
+
+def nvfp4_decode_weight_bytes(rows: int, cols: int) -> int:
+    return int(load().nvfp4_decode_weight_bytes(rows, cols))
+
+
+def nvfp4_decode_weight_pack(w: NVFP4Tensor, packed: torch.Tensor, stream=None) -> None:
+    """C ``nvfp4_decode_weight_pack``: w (row-major NVFP4) into the decode layout."""
+    dw = w.descriptor()
+    st = load().nvfp4_decode_weight_pack(ctypes.byref(dw), packed.data_ptr(), packed.numel() * packed.element_size(),
+                                         _stream(w.codes.device, stream))
+    _check(st, "nvfp4_decode_weight_pack")
+
+
+def nvfp4_gemm_decode(a: NVFP4Tensor, w: DecodeWeight, seg_offsets, seg_global_scales: torch.Tensor,
+                      out: torch.Tensor, gate: dict | None = None, stream=None) -> None:
+    """C ``nvfp4_gemm_decode``: ``nvfp4_gemm_fused_segments`` for a packed
+    weight and at most 16 activation rows."""
+    _check_dense(out, a.rows, w.rows, a.codes.device, "out")
+    offs = (ctypes.c_int64 * len(seg_offsets))(*[int(o) for o in seg_offsets])
+    g = _gate(gate)
+    da, dw = a.descriptor(), w.descriptor()
+    st = load().nvfp4_gemm_decode(ctypes.byref(da), ctypes.byref(dw), len(seg_offsets) - 1, offs,
+                                  seg_global_scales.data_ptr(), None if g is None else ctypes.byref(g),
+                                  out.data_ptr(), _dtype_code(out), out.stride(0), _stream(out.device, stream))
+    _check(st, "nvfp4_gemm_decode")
+
+
+def nvfp4_linear_decode(x: torch.Tensor, w: DecodeWeight, seg_offsets, seg_global_scales: torch.Tensor,
+                        out: torch.Tensor, x_global_scale: torch.Tensor | None = None, gate: dict | None = None,
+                        stream=None) -> None:
+    """C ``nvfp4_linear_decode``: dense x (<= 16 rows) quantized inside the
+    launch, then the packed-weight GEMM."""
+    if x.dim() != 2 or x.stride(1) != 1 or x.shape[1] != w.cols:
+        raise NVFP4Error(f"x must be [rows, {w.cols}] with contiguous rows")
+    _check_dense(out, x.shape[0], w.rows, x.device, "out")
+    offs = (ctypes.c_int64 * len(seg_offsets))(*[int(o) for o in seg_offsets])
+    g = _gate(gate)
+    dw = w.descriptor()
+    st = load().nvfp4_linear_decode(x.data_ptr(), _dtype_code(x), x.shape[0], x.stride(0), _ptr(x_global_scale),
+                                    ctypes.byref(dw), len(seg_offsets) - 1, offs, seg_global_scales.data_ptr(),
+                                    None if g is None else ctypes.byref(g), out.data_ptr(), _dtype_code(out),
+                                    out.stride(0), _stream(out.device, stream))
+    _check(st, "nvfp4_linear_decode")
+
+
 def nvfp4_silu_mul(gu: torch.Tensor, h: torch.Tensor, inter: int, amax_workspace: torch.Tensor | None = None,
                    stream=None) -> None:
     """C ``nvfp4_silu_mul``: h = bf16(silu(gu[:, :inter]) * gu[:, inter:2*inter])."""
+    if gu.dim() != 2 or gu.stride(1) != 1 or gu.shape[1] < 2 * inter:
+        raise NVFP4Error(f"gu must be [rows, >= {2 * inter}] with contiguous rows")
+    _check_dense(h, gu.shape[0], inter, gu.device, "h")
     ws_bytes = 0 if amax_workspace is None else amax_workspace.numel() * amax_workspace.element_size()
     st = load().nvfp4_silu_mul(gu.data_ptr(), gu.shape[0], inter, gu.stride(0), h.data_ptr(), h.stride(0),
                                _ptr(amax_workspace), ws_bytes, _stream(gu.device, stream))
@@ -247,6 +354,11 @@ def nvfp4_gemm_swiglu(a: NVFP4Tensor, w_gate_up: NVFP4Tensor, seg_global_scales:
     """C ``nvfp4_gemm_swiglu``: h = bf16(silu(gate) * up) from one GEMM over
     w_gate_up = [gate; up] (2 segments), written as bf16 ``h`` and/or as
     NVFP4 ``h_q`` quantized with the static scale already in h_q.global_scale."""
+    inter = w_gate_up.rows // 2
+    if h is not None:
+        _check_dense(h, a.rows, inter, a.codes.device, "h")
+    if h_q is not None:
+        _check_nvfp4(h_q, a.rows, inter, a.codes.device, "h_q")
     ws_bytes = 0 if amax_workspace is None else amax_workspace.numel() * amax_workspace.element_size()
     da, dw = a.descriptor(), w_gate_up.descriptor()
     dq = None if h_q is None else h_q.descriptor()
@@ -355,6 +467,31 @@ def gemm_fused_segments(a: NVFP4Tensor, w: NVFP4Tensor, seg_offsets, seg_global_
                         gate: dict | None = None, out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
     o = out if out is not None else torch.empty((a.rows, w.rows), dtype=out_dtype, device=a.codes.device)
     nvfp4_gemm_fused_segments(a, w, seg_offsets, seg_global_scales, o, gate)
+    return o
+
+
+def pack_decode(w: NVFP4Tensor) -> DecodeWeight:
+    """The decode-layout copy of an NVFP4 weight (offline, like quantization)."""
+    nbytes = nvfp4_decode_weight_bytes(w.rows, w.cols)
+    if nbytes == 0:
+        raise NVFP4Error(f"a [{w.rows}, {w.cols}] weight has no decode layout (cols <= 8192, % 16)")
+    data = torch.empty(nbytes, dtype=torch.uint8, device=w.codes.device)
+    nvfp4_decode_weight_pack(w, data)
+    return DecodeWeight(data, w.rows, w.cols)
+
+
+def gemm_decode(a: NVFP4Tensor, w: DecodeWeight, seg_offsets, seg_global_scales: torch.Tensor,
+                gate: dict | None = None, out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    o = out if out is not None else torch.empty((a.rows, w.rows), dtype=out_dtype, device=a.codes.device)
+    nvfp4_gemm_decode(a, w, seg_offsets, seg_global_scales, o, gate)
+    return o
+
+
+def linear_decode(x: torch.Tensor, w: DecodeWeight, seg_offsets, seg_global_scales: torch.Tensor,
+                  gate: dict | None = None, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                  x_global_scale: torch.Tensor | None = None) -> torch.Tensor:
+    o = out if out is not None else torch.empty((x.shape[0], w.rows), dtype=out_dtype, device=x.device)
+    nvfp4_linear_decode(x, w, seg_offsets, seg_global_scales, o, x_global_scale, gate)
     return o
 
 

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_skinny.hip", "glue.hip", "kv_fp8.hip", "harmonize.hip",
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_skinny.hip", "gemm_decode.hip", "glue.hip", "kv_fp8.hip", "harmonize.hip",
            "gdn.hip", "noalloc.hip"]
 LIB = os.path.join(PKG, "libnvfp4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -44,6 +44,41 @@ int check_out(const void* out, int out_dtype, int64_t ld_out, int64_t n) {
   return NVFP4_OK;
 }
 
+// Segment table and gate of a fused GEMM into the epilogue arguments.
+int fill_segments(int n_segments, const int64_t* seg_offsets, const float* seg_global_scales,
+                  const nvfp4_gdn_gate* gate, int64_t n, EpilogueArgs& ep) {
+  if (n_segments < 1 || n_segments > NVFP4_MAX_SEGMENTS) return NVFP4_ERR_SEGMENTS;
+  if (seg_offsets == nullptr || seg_global_scales == nullptr) return NVFP4_ERR_NULL;
+  if (seg_offsets[0] != 0 || seg_offsets[n_segments] != n) return NVFP4_ERR_SEGMENTS;
+  for (int s = 0; s < n_segments; ++s)
+    if (seg_offsets[s + 1] <= seg_offsets[s]) return NVFP4_ERR_SEGMENTS;
+  ep.n_seg = n_segments;
+  for (int s = 0; s <= n_segments; ++s) ep.seg_off[s] = (int)seg_offsets[s];
+  ep.seg_g = seg_global_scales;
+  ep.b_seg = -1;
+  ep.a_seg = -1;
+  if (gate != nullptr) {
+    const int bs = gate->b_segment, as = gate->a_segment;
+    if (bs < -1 || bs >= n_segments || as < -1 || as >= n_segments) return NVFP4_ERR_GATE;
+    if (bs >= 0 && bs == as) return NVFP4_ERR_GATE;
+    if (as >= 0 && (gate->A_log == nullptr || gate->dt_bias == nullptr)) return NVFP4_ERR_GATE;
+    ep.b_seg = bs;
+    ep.a_seg = as;
+    ep.A_log = gate->A_log;
+    ep.dt_bias = gate->dt_bias;
+  }
+  return NVFP4_OK;
+}
+
+int check_decode_weight(const nvfp4_decode_weight* w) {
+  if (w == nullptr || w->data == nullptr) return NVFP4_ERR_NULL;
+  if (w->rows <= 0 || w->cols <= 0 || w->cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (w->rows >= kIndexLimit) return NVFP4_ERR_RANGE;
+  if (w->cols > kDecodeMaxK) return NVFP4_ERR_SHAPE;
+  if (!aligned(w->data, 16)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 namespace nvfp4 {
@@ -375,6 +410,78 @@ int nvfp4_gdn_recurrence(const nvfp4_gdn_inputs* in, int in_dtype, int64_t token
   p.ld_o = ld_o;
   p.o_dtype = o_dtype;
   return hip_status(launch_gdn(p, (float*)workspace, (hipStream_t)stream));
+}
+
+size_t nvfp4_decode_weight_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || cols > kDecodeMaxK || rows >= kIndexLimit) return 0;
+  return decode_weight_bytes(rows, cols);
+}
+
+int nvfp4_decode_weight_pack(const nvfp4_tensor* w, void* packed, size_t packed_bytes, void* stream) {
+  const int st = check_tensor(w);
+  if (st != NVFP4_OK) return st;
+  if (packed == nullptr) return NVFP4_ERR_NULL;
+  if (w->cols > kDecodeMaxK) return NVFP4_ERR_SHAPE;
+  if (!aligned(packed, 16)) return NVFP4_ERR_ALIGN;
+  if (packed_bytes < decode_weight_bytes(w->rows, w->cols)) return NVFP4_ERR_WORKSPACE;
+  return hip_status(launch_decode_pack(w->codes, w->ld_codes, w->scales, w->ld_scales, (int)w->rows,
+                                       (int)w->cols, (uint8_t*)packed, (hipStream_t)stream));
+}
+
+int nvfp4_gemm_decode(const nvfp4_tensor* a, const nvfp4_decode_weight* w, int n_segments,
+                      const int64_t* seg_offsets, const float* seg_global_scales, const nvfp4_gdn_gate* gate,
+                      void* out, int out_dtype, int64_t ld_out, void* stream) {
+  int st = check_tensor(a);
+  if (st != NVFP4_OK) return st;
+  st = check_decode_weight(w);
+  if (st != NVFP4_OK) return st;
+  if (a->global_scale == nullptr) return NVFP4_ERR_NULL;
+  if (a->cols != w->cols || a->rows > kDecodeMaxM) return NVFP4_ERR_SHAPE;
+  st = check_out(out, out_dtype, ld_out, w->rows);
+  if (st != NVFP4_OK) return st;
+  GemmArgs p{};
+  st = fill_segments(n_segments, seg_offsets, seg_global_scales, gate, w->rows, p.ep);
+  if (st != NVFP4_OK) return st;
+  p.a_codes = a->codes;
+  p.a_scales = a->scales;
+  p.lda_c = a->ld_codes;
+  p.lda_s = a->ld_scales;
+  p.ep.a_g = a->global_scale;
+  p.out = out;
+  p.ld_out = ld_out;
+  p.out_bf16 = out_dtype == NVFP4_DTYPE_BF16;
+  p.M = (int)a->rows;
+  p.N = (int)w->rows;
+  p.K = (int)w->cols;
+  return hip_status(launch_gemm_decode(p, (const uint8_t*)w->data, nullptr, 0, 0, nullptr, p.ep.b_seg >= 0 ||
+                                       p.ep.a_seg >= 0, (hipStream_t)stream));
+}
+
+int nvfp4_linear_decode(const void* x, int x_dtype, int64_t rows, int64_t ld_x, float* x_global_scale,
+                        const nvfp4_decode_weight* w, int n_segments, const int64_t* seg_offsets,
+                        const float* seg_global_scales, const nvfp4_gdn_gate* gate, void* out, int out_dtype,
+                        int64_t ld_out, void* stream) {
+  if (x == nullptr) return NVFP4_ERR_NULL;
+  int st = check_decode_weight(w);
+  if (st != NVFP4_OK) return st;
+  if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || rows > kDecodeMaxM) return NVFP4_ERR_SHAPE;
+  const int esz = x_dtype == NVFP4_DTYPE_BF16 ? 2 : 4;
+  if (ld_x < w->cols || (ld_x * esz) % 16 != 0) return NVFP4_ERR_STRIDE;
+  if (!aligned(x, 16) || !aligned(x_global_scale, 4)) return NVFP4_ERR_ALIGN;
+  st = check_out(out, out_dtype, ld_out, w->rows);
+  if (st != NVFP4_OK) return st;
+  GemmArgs p{};
+  st = fill_segments(n_segments, seg_offsets, seg_global_scales, gate, w->rows, p.ep);
+  if (st != NVFP4_OK) return st;
+  p.out = out;
+  p.ld_out = ld_out;
+  p.out_bf16 = out_dtype == NVFP4_DTYPE_BF16;
+  p.M = (int)rows;
+  p.N = (int)w->rows;
+  p.K = (int)w->cols;
+  return hip_status(launch_gemm_decode(p, (const uint8_t*)w->data, x, x_dtype, ld_x, x_global_scale,
+                                       p.ep.b_seg >= 0 || p.ep.a_seg >= 0, (hipStream_t)stream));
 }
 
 const char* nvfp4_status_string(int status) {

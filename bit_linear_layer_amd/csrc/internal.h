@@ -110,6 +110,18 @@ hipError_t launch_harmonize(const uint8_t* in, int64_t ld_in, uint8_t* out, int6
 bool skinny_eligible(const GemmArgs& p);
 hipError_t launch_gemm_skinny(const GemmArgs& p, int n_lo, int n_hi, bool gate, hipStream_t s);
 
+// Decode GEMM on a weight in the decode layout (gemm_decode.hip): M <= 16,
+// K <= kDecodeMaxK.  Activations pre-quantized (g.a_codes, ...) or, with x
+// non-null, dense x quantized inside the launch (its dynamic global scale
+// written to x_g_out when non-null).
+constexpr int64_t kDecodeMaxK = 8192;
+constexpr int64_t kDecodeMaxM = 16;
+size_t decode_weight_bytes(int64_t N, int64_t K);
+hipError_t launch_decode_pack(const uint8_t* codes, int64_t ldc, const uint8_t* scales, int64_t lds, int N, int K,
+                              uint8_t* out, hipStream_t s);
+hipError_t launch_gemm_decode(const GemmArgs& g, const uint8_t* packed, const void* x, int x_dtype, int64_t ld_x,
+                              float* x_g_out, bool gate, hipStream_t s);
+
 // Gated delta-rule recurrence (gdn.hip).
 struct GdnArgs {
   const void* q; int64_t ld_q;

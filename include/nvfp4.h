@@ -198,6 +198,64 @@ int nvfp4_gemm_fused_segments(const nvfp4_tensor* a, const nvfp4_tensor* w, int 
                               void* stream);
 
 /*
+ * Decode (M <= 16 tokens): the weight streams from HBM once per call, so it
+ * is bound by bandwidth, and the row-major layout above (16 rows of one
+ * MFMA operand in 16 places) costs the memory path more than the bytes.
+ * For this regime a weight is repacked once, offline like its
+ * quantization (chatpaper.ai English abstract: weights quantized per
+ * module, activations on every call), into the decode layout: for each 16
+ * rows and each of 8 K slices, one contiguous unit in which every 1 KB is
+ * one wavefront-wide load, already in MFMA operand order.  The layout is
+ * internal to this library (its size from nvfp4_decode_weight_bytes); the
+ * values are the row-major tensor's codes and scales, zero-padded to whole
+ * 16-row groups and K slices.
+ */
+typedef struct {
+  const void* data; /* device, nvfp4_decode_weight_bytes(rows, cols) bytes, 16-byte aligned */
+  int64_t rows, cols;
+} nvfp4_decode_weight;
+
+/* Bytes of a [rows, cols] weight in the decode layout; 0 for a shape the
+ * decode path does not take (cols % 16 != 0 or cols > 8192). */
+size_t nvfp4_decode_weight_bytes(int64_t rows, int64_t cols);
+
+/*
+ * nvfp4_decode_weight_pack -- write w (row-major NVFP4, as nvfp4_quantize
+ * leaves it) into the decode layout at `packed` (device, >=
+ * nvfp4_decode_weight_bytes(w->rows, w->cols) bytes, 16-byte aligned;
+ * NVFP4_ERR_WORKSPACE if shorter).  w->global_scale is not used: global
+ * scales are passed to the GEMM.  cols <= 8192.
+ */
+int nvfp4_decode_weight_pack(const nvfp4_tensor* w, void* packed, size_t packed_bytes, void* stream);
+
+/*
+ * nvfp4_gemm_decode -- nvfp4_gemm_fused_segments for a weight in the decode
+ * layout and a->rows <= 16: the same arguments, the same per-segment global
+ * scales and gate epilogue, the same exact decode and fp32 MFMA
+ * accumulation (outputs agree with nvfp4_gemm_fused_segments within the
+ * same 1e-5 * sum|a*w| bound; the summation order differs).
+ */
+int nvfp4_gemm_decode(const nvfp4_tensor* a, const nvfp4_decode_weight* w, int n_segments,
+                      const int64_t* seg_offsets, const float* seg_global_scales,
+                      const nvfp4_gdn_gate* gate, void* out, int out_dtype, int64_t ld_out, void* stream);
+
+/*
+ * nvfp4_linear_decode -- the whole W4A4 linear layer at decode in one
+ * launch: dense activations x [rows, w->cols] (bf16 or float32, rows <= 16,
+ * row stride ld_x elements, rows 16-byte aligned) are NVFP4-quantized with
+ * their dynamic global scale inside the launch -- codes, scales and g bit
+ * for bit those of nvfp4_quantize(x, NVFP4_SCALE_DYNAMIC) -- and multiplied
+ * with the packed weight as nvfp4_gemm_decode does; the output is bit for
+ * bit that of nvfp4_quantize followed by nvfp4_gemm_decode.
+ *   x_global_scale  device float32[1] receiving x's global scale, or NULL.
+ * Other arguments as nvfp4_gemm_decode.
+ */
+int nvfp4_linear_decode(const void* x, int x_dtype, int64_t rows, int64_t ld_x, float* x_global_scale,
+                        const nvfp4_decode_weight* w, int n_segments, const int64_t* seg_offsets,
+                        const float* seg_global_scales, const nvfp4_gdn_gate* gate, void* out,
+                        int out_dtype, int64_t ld_out, void* stream);
+
+/*
  * nvfp4_silu_mul -- MLP glue between the gate_up and down projections:
  *   h[m, j] = bf16( silu(gu[m, j]) * gu[m, inter + j] ),  j < inter,
  * evaluated in fp32 from bf16 inputs, rounded to nearest even.

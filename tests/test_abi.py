@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import bit_linear_layer_amd as nv
 
@@ -194,3 +195,75 @@ def qn(**kw):
 def test_quantize_noalloc_rejects_bad_arguments(kw, status):
     assert qn(**kw) == status
 
+
+def test_decode_weight_bytes():
+    # 2176 groups x 8 K slices x (5 chunks x 1152 bytes): exactly the codes
+    # and scales of a 34816 x 5120 weight
+    assert nv.nvfp4_decode_weight_bytes(34816, 5120) == 34816 * 5120 // 2 + 34816 * 5120 // 16
+    assert nv.nvfp4_decode_weight_bytes(1, 16) == 8 * 1152
+    assert nv.nvfp4_decode_weight_bytes(1, 8208) == 0
+    assert nv.nvfp4_decode_weight_bytes(1, 24) == 0
+    assert nv.nvfp4_decode_weight_bytes(0, 16) == 0
+
+
+def gemm_decode(a=None, w=None, n_seg=1, offs=None, out=FAKE, dt=0, ld=8, gate=None):
+    a = a or tensor()
+    w = w or nv._DecodeWeight(FAKE, 8, 32)
+    offs = offs or [0, w.rows]
+    arr = (ctypes.c_int64 * len(offs))(*offs)
+    return nv.load().nvfp4_gemm_decode(ctypes.byref(a), ctypes.byref(w), n_seg, arr, FAKE,
+                                       None if gate is None else ctypes.byref(gate), out, dt, ld, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a=tensor(rows=17)), -2), (dict(a=tensor(cols=48, ldc=32, lds=8)), -2),
+    (dict(w=nv._DecodeWeight(None, 8, 32)), -1), (dict(w=nv._DecodeWeight(FAKE + 8, 8, 32)), -5),
+    (dict(w=nv._DecodeWeight(FAKE, 8, 8208)), -2), (dict(out=None), -1), (dict(ld=4), -4),
+    (dict(offs=[0, 4]), -6), (dict(n_seg=0), -6), (dict(dt=5), -3),
+    (dict(gate=nv._Gate(0, 0, FAKE, FAKE)), -7),
+])
+def test_gemm_decode_rejects_bad_arguments(kw, status):
+    assert gemm_decode(**kw) == status
+
+
+def linear_decode(x=FAKE, dt=0, rows=8, ldx=32, w=None, out=FAKE, ld=8):
+    w = w or nv._DecodeWeight(FAKE, 8, 32)
+    arr = (ctypes.c_int64 * 2)(0, w.rows)
+    return nv.load().nvfp4_linear_decode(x, dt, rows, ldx, None, ctypes.byref(w), 1, arr, FAKE, None, out, 0,
+                                         ld, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), -1), (dict(rows=17), -2), (dict(rows=0), -2), (dict(dt=3), -3),
+    (dict(ldx=24), -4), (dict(ldx=36), -4), (dict(x=FAKE + 2), -5), (dict(out=None), -1),
+])
+def test_linear_decode_rejects_bad_arguments(kw, status):
+    assert linear_decode(**kw) == status
+
+
+def cpu_nvfp4(rows, cols):
+    ldc = max(16, (cols // 2 + 15) // 16 * 16)
+    lds = max(16, (cols // 16 + 15) // 16 * 16)
+    return nv.NVFP4Tensor(torch.zeros((rows, ldc), dtype=torch.uint8), torch.zeros((rows, lds), dtype=torch.uint8),
+                          torch.zeros(1), rows, cols)
+
+
+@pytest.mark.parametrize("out", [torch.zeros((4, 7)), torch.zeros((5, 8)), torch.zeros((8, 4)).t(),
+                                 torch.zeros((4, 8), dtype=torch.float64)])
+def test_binding_rejects_bad_outputs(out):
+    """The binding checks caller-supplied outputs before calling the library:
+    wrong shape, non-contiguous rows, or (here, on the CPU) a host tensor."""
+    a, w = cpu_nvfp4(4, 32), cpu_nvfp4(8, 32)
+    with pytest.raises(nv.NVFP4Error):
+        nv.nvfp4_gemm(a, w, out)
+    with pytest.raises(nv.NVFP4Error):
+        nv.nvfp4_gemm_fused_segments(a, w, [0, 8], torch.zeros(1), out)
+
+
+def test_binding_rejects_mismatched_quantize_target():
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    for q in (cpu_nvfp4(5, 32), cpu_nvfp4(4, 48), cpu_nvfp4(4, 32)):
+        with pytest.raises(nv.NVFP4Error):
+            nv.nvfp4_quantize(x, q, nv.SCALE_DYNAMIC, torch.zeros(1))
+    with pytest.raises(nv.NVFP4Error):
+        nv.nvfp4_quantize(torch.zeros((4, 32)).t(), cpu_nvfp4(32, 4))
