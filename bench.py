@@ -34,6 +34,8 @@ METRIC = "NVFP4 W4A4 GEMM TFLOP/s incl. act-quant (M=8192) + % peak; GB/s at M=8
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_m8192_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_m8192_mfma.json")
+NOMINAL_CLOCK_GHZ = 2.4
 # sources the gate|up GEMM kernel is compiled from: the committed HBM
 # counters are reported only while all of them are unchanged
 GEMM_SRC = [os.path.join(ROOT, "bit_linear_layer_amd", "csrc", f)
@@ -75,6 +77,20 @@ def read_traffic():
     if t.get("gemm_source_sha256") != sha256(GEMM_SRC):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def read_mfma_counters():
+    """Observed shader clock and MFMA-busy fraction of the gate|up GEMM from
+    the committed rocprofv3 counter summary, or None if absent or taken on
+    another kernel source."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256") != sha256(GEMM_SRC):
+        return None
+    return t
 
 
 def main():
@@ -194,6 +210,16 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / MFMA_F16_PEAK_TFLOPS, 2),
         "roofline": roofline,
     }
+    mc = read_mfma_counters()
+    if mc is not None:
+        clk = mc["observed_clock_ghz"]
+        result["clock"] = {
+            "observed_ghz": clk, "nominal_ghz": NOMINAL_CLOCK_GHZ,
+            "source": "rocprofv3 GRBM_GUI_ACTIVE / 8 XCDs / duration of the gate|up GEMM "
+                      "(profiles/gemm_gate_up_m8192_mfma.json)",
+            "pct_of_mfma_peak_at_observed_clock": round(
+                100.0 * value / (MFMA_F16_PEAK_TFLOPS * clk / NOMINAL_CLOCK_GHZ), 2),
+            "gate_up_mfma_busy_frac": mc["mfma_busy_frac"]}
 
     # --------------------------------------------- decode shape (M = 8)
     if not args.no_secondary:
