@@ -123,3 +123,30 @@ def test_kv_full_size_write_and_read():
     q = O.kv_fp8_quantize(xf, s_ref)
     assert np.array_equal(cache.cpu().numpy(), q)
     assert np.array_equal(W.bf16_to_f32_numpy(back).astype(np.float64), O.kv_fp8_dequantize(q, s_ref, "bf16"))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_kv_cache_rows_8_byte_aligned(dtype):
+    """A cache whose rows start 8 (not 16) bytes apart: the write stores in
+    8-byte halves and the read loads them the same way; the padding bytes of
+    each row stay untouched, and the bytes equal those of a dense cache."""
+    say(f"kv fp8 cache rows 8-byte aligned {dtype}")
+    rng = np.random.default_rng(21)
+    rows, cols = 333, 272
+    x = torch.from_numpy((rng.standard_normal((rows, cols)) * 7).astype(np.float32)).to(dtype).to(DEV)
+    sc = nv.kv_fp8_calibrate(x)
+    dense = nv.kv_fp8_quantize(x, sc)
+    big = torch.full((rows, cols + 8), 0xA5, dtype=torch.uint8, device=DEV)
+    nv.nvfp4_kv_fp8_quantize(x, big[:, :cols], sc)
+    torch.cuda.synchronize()
+    assert big.stride(0) % 16 == 8
+    xf = x.float().cpu().numpy()
+    assert np.array_equal(dense.cpu().numpy(), O.kv_fp8_quantize(xf, np.float32(sc.cpu().numpy()[0])))
+    assert torch.equal(big[:, :cols], dense)
+    assert bool((big[:, cols:] == 0xA5).all())
+    out_dense = nv.kv_fp8_dequantize(dense, sc, out_dtype=dtype)
+    out = torch.empty((rows, cols), dtype=dtype, device=DEV)
+    nv.nvfp4_kv_fp8_dequantize(big[:, :cols], sc, out, cols)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       out_dense.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
