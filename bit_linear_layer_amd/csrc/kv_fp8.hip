@@ -208,9 +208,13 @@ __global__ __launch_bounds__(kElemThreads) void kv_scale_kernel(const float* __r
   }
 }
 
+// At most 2048 workgroups (8 per CU on 256 CUs, all resident at once),
+// each thread walking several chunks: measured faster than 8192 or 32768
+// workgroups with fewer chunks each (32768 x 1024 bf16: write 27.3 -> 25.9
+// us calibrated, read 22.9 -> 20.6 us), and than 1024 or 1536.
 int chunk_grid(int64_t chunks) {
   int64_t wg = (chunks + kElemThreads - 1) / kElemThreads;
-  if (wg > 8192) wg = 8192;
+  if (wg > 2048) wg = 2048;
   if (wg < 1) wg = 1;
   return (int)wg;
 }
