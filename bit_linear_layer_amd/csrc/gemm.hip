@@ -319,7 +319,7 @@ __device__ inline void store_staged_tile(const uint8_t* tile, int m0, int n0, in
     const uint4 v = *reinterpret_cast<const uint4*>(tile + row * staged_row_bytes<COLS>() + col * 2);
     uint16_t* dst = out + (int64_t)m * ld_out + n;
     if (n + 8 <= n_hi) {
-      *reinterpret_cast<uint4*>(dst) = v;
+      store_stream16(dst, v.x, v.y, v.z, v.w);
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       for (int q = 0; q < 8 && n + q < n_hi; ++q) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
@@ -436,8 +436,8 @@ __device__ __attribute__((always_inline)) inline void swiglu_epilogue(
       }
       uint2 c;
       const uint32_t sc = quantize_block16(v, gh, &c);
-      *reinterpret_cast<uint2*>(p.ep.hq_codes + (int64_t)m * p.ep.hq_ld_codes + h0 / 2) = c;
-      p.ep.hq_scales[(int64_t)m * p.ep.hq_ld_scales + h0 / 16] = (uint8_t)sc;
+      store_stream8(p.ep.hq_codes + (int64_t)m * p.ep.hq_ld_codes + h0 / 2, c.x, c.y);
+      store_stream1(p.ep.hq_scales + (int64_t)m * p.ep.hq_ld_scales + h0 / 16, (uint8_t)sc);
     }
   }
 }

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kElemThreads) void silu_mul_kernel(
       hw[i] = b0 | (b1 << 16);
       m = fmaxf(m, fmaxf(__uint_as_float((b0 & 0x7FFFu) << 16), __uint_as_float((b1 & 0x7FFFu) << 16)));
     }
-    *reinterpret_cast<uint4*>(h + r * ld_h + c * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    dev::store_stream16(h + r * ld_h + c * 8, hw[0], hw[1], hw[2], hw[3]);
   }
   if (partials != nullptr) {
     __shared__ float red[kElemThreads / 64];

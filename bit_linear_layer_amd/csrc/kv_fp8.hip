@@ -56,12 +56,12 @@ __device__ inline void load8(const uint8_t* p, float v[8]) {
   }
 }
 
-// Grid-stride walk over [rows, cpr] 8-element chunks.
+// Walk over the 8-element chunks of a [rows, cpr] matrix from chunk `start`
+// in steps of `stride` chunks, keeping (row, chunk-in-row) without a division
+// per step.
 struct ChunkWalk {
   int64_t r, c, cpr, rows, dr, dc;
-  __device__ ChunkWalk(int64_t rows_, int64_t cpr_) : cpr(cpr_), rows(rows_) {
-    const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  __device__ ChunkWalk(int64_t rows_, int64_t cpr_, int64_t start, int64_t stride) : cpr(cpr_), rows(rows_) {
     r = start / cpr;
     c = start - r * cpr;
     dr = stride / cpr;
@@ -77,6 +77,15 @@ struct ChunkWalk {
     }
   }
 };
+
+// Each thread takes two chunks per iteration, one grid-width apart (so every
+// load instruction of a wavefront still reads contiguous bytes), and issues
+// both loads before converting either.  The cache and output bytes go out as
+// streaming stores.  Measured against one chunk per iteration and plain
+// stores, 32768 x 1024 bf16: unit-scale write 21.7 -> 16.8 us, calibrated
+// write 25.7 -> 22.7 us, bf16 read 20.3 -> 16.6 us; four chunks per
+// iteration, or fewer workgroups, were slower.
+constexpr int kChunksPerIter = 2;
 
 // Magnitude of the E4M3 byte P of `src`, decoded by the hardware conversion (exact).
 template <int P>
@@ -144,26 +153,41 @@ __global__ __launch_bounds__(kElemThreads) void kv_quant_kernel(
   const float R = 1.0f / sf;
   const float r_lo = R * (1.0f - 0x1p-18f), r_hi = R * (1.0f + 0x1p-18f);
   const double s = (double)sf;
-  for (ChunkWalk it(rows, cpr); it.valid(); it.next()) {
-    const int64_t dst = slots != nullptr ? slots[it.r] : it.r;
-    if (dst < 0 || dst >= cache_rows) continue;  // documented: such rows are not written
-    float v[8];
-    load8<DT>(x + it.r * ld_bytes + it.c * kChunkBytes, v);
-    uint32_t w[2] = {0u, 0u};
-    if (pow2) {
-      w[0] = e4m3_quad_exact(v, R);
-      w[1] = e4m3_quad_exact(v + 4, R);
-    } else if (fast) {
-      w[0] = e4m3_quad(v, r_lo, r_hi, sf);
-      w[1] = e4m3_quad(v + 4, r_lo, r_hi, sf);
-    } else {
+  constexpr int U = kChunksPerIter;
+  static_assert(U == 2, "the walkers below are listed one by one");
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  ChunkWalk it[U] = {ChunkWalk(rows, cpr, start, U * T), ChunkWalk(rows, cpr, start + T, U * T)};
+  while (it[0].valid()) {
+    float v[U][8];
+    int64_t dst[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t m = e4m3_rne((double)fabsf(v[e]) / s);
-        w[e >> 2] |= (m | ((__float_as_uint(v[e]) >> 31) << 7)) << (8 * (e & 3));
-      }
+    for (int j = 0; j < U; ++j) {
+      const bool ok = it[j].valid();
+      dst[j] = ok ? (slots != nullptr ? slots[it[j].r] : it[j].r) : -1;
+      if (ok) load8<DT>(x + it[j].r * ld_bytes + it[j].c * kChunkBytes, v[j]);
     }
-    *reinterpret_cast<uint2*>(cache + dst * ld_cache + it.c * 8) = make_uint2(w[0], w[1]);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (dst[j] < 0 || dst[j] >= cache_rows) continue;  // documented: such rows are not written
+      uint32_t w[2] = {0u, 0u};
+      if (pow2) {
+        w[0] = e4m3_quad_exact(v[j], R);
+        w[1] = e4m3_quad_exact(v[j] + 4, R);
+      } else if (fast) {
+        w[0] = e4m3_quad(v[j], r_lo, r_hi, sf);
+        w[1] = e4m3_quad(v[j] + 4, r_lo, r_hi, sf);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t m = e4m3_rne((double)fabsf(v[j][e]) / s);
+          w[e >> 2] |= (m | ((__float_as_uint(v[j][e]) >> 31) << 7)) << (8 * (e & 3));
+        }
+      }
+      store_stream8(cache + dst[j] * ld_cache + it[j].c * 8, w[0], w[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) it[j].next();
   }
 }
 
@@ -172,23 +196,35 @@ __global__ __launch_bounds__(kElemThreads) void kv_dequant_kernel(
     const uint8_t* __restrict__ cache, int64_t ld_cache, int64_t rows, int64_t cpr,
     const float* __restrict__ scale, uint8_t* __restrict__ out, int64_t ld_out_bytes) {
   const float s = *scale;
-  for (ChunkWalk it(rows, cpr); it.valid(); it.next()) {
-    const uint2 q = *reinterpret_cast<const uint2*>(cache + it.r * ld_cache + it.c * 8);
-    float f[8];
-    const f32x2_t d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false), d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
-    const f32x2_t d2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false), d3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
-    f[0] = d0.x * s; f[1] = d0.y * s; f[2] = d1.x * s; f[3] = d1.y * s;
-    f[4] = d2.x * s; f[5] = d2.y * s; f[6] = d3.x * s; f[7] = d3.y * s;
-    if constexpr (OUT == NVFP4_DTYPE_BF16) {
-      uint32_t h[4];
+  constexpr int U = kChunksPerIter;
+  static_assert(U == 2, "the walkers below are listed one by one");
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  ChunkWalk it[U] = {ChunkWalk(rows, cpr, start, U * T), ChunkWalk(rows, cpr, start + T, U * T)};
+  while (it[0].valid()) {
+    uint2 q[U];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-      *reinterpret_cast<uint4*>(out + it.r * ld_out_bytes + it.c * 16) = make_uint4(h[0], h[1], h[2], h[3]);
-    } else {
-      float4* o = reinterpret_cast<float4*>(out + it.r * ld_out_bytes + it.c * 32);
-      o[0] = make_float4(f[0], f[1], f[2], f[3]);
-      o[1] = make_float4(f[4], f[5], f[6], f[7]);
+    for (int j = 0; j < U; ++j)
+      if (it[j].valid()) q[j] = *reinterpret_cast<const uint2*>(cache + it[j].r * ld_cache + it[j].c * 8);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (!it[j].valid()) continue;
+      float f[8];
+      const f32x2_t d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[j].x, false), d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[j].x, true);
+      const f32x2_t d2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[j].y, false), d3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[j].y, true);
+      f[0] = d0.x * s; f[1] = d0.y * s; f[2] = d1.x * s; f[3] = d1.y * s;
+      f[4] = d2.x * s; f[5] = d2.y * s; f[6] = d3.x * s; f[7] = d3.y * s;
+      if constexpr (OUT == NVFP4_DTYPE_BF16) {
+        store_stream16(out + it[j].r * ld_out_bytes + it[j].c * 16, pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+      } else {
+        uint8_t* o = out + it[j].r * ld_out_bytes + it[j].c * 32;
+        store_stream16(o, __float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+        store_stream16(o + 16, __float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7]));
+      }
     }
+#pragma unroll
+    for (int j = 0; j < U; ++j) it[j].next();
   }
 }
 

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_util.h"
 #include "internal.h"
 #include "quant_block.h"
 
@@ -160,8 +161,8 @@ __global__ __launch_bounds__(kElemThreads) void quantize_kernel(
     cur.to_float(v);
     uint2 c;
     const uint32_t s = dev::quantize_block16(v, g, &c);
-    *reinterpret_cast<uint2*>(codes + it.r * ld_codes + it.j * 8) = c;
-    scales[it.r * ld_scales + it.j] = (uint8_t)s;
+    dev::store_stream8(codes + it.r * ld_codes + it.j * 8, c.x, c.y);
+    dev::store_stream1(scales + it.r * ld_scales + it.j, (uint8_t)s);
     if (!more) break;
     cur = nb;
     it = nx;
