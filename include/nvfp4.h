@@ -327,6 +327,7 @@ int nvfp4_kv_fp8_calibrate(const void* x, int x_dtype, int64_t rows, int64_t col
  * ties to even code, |x / s| beyond 448 saturating to +-448, sign bit = IEEE
  * sign of x.  slot(i) = slots[i] (DEVICE int64 [rows]) or i when slots is
  * NULL; rows whose slot lies outside [0, cache_rows) are not written.
+ * x must be finite: a NaN element gets an unspecified byte.
  * cache: DEVICE uint8 [cache_rows, ld_cache], ld_cache % 8 == 0, 8-byte
  * aligned; x rows 16-byte aligned.
  */

@@ -71,7 +71,7 @@ def test_streaming_outputs_use_nontemporal_stores(disassembly):
         return found
 
     # the FP8 KV cache and its read-back: every store streams
-    for part in ("kv_quant_kernel", "kv_dequant_kernel"):
+    for part in ("kv_quant_kernel", "kv_quant_linear_kernel", "kv_dequant_kernel"):
         for name, st in stores(part).items():
             assert st and all(re.search(r"\bnt\b", l) for l in st), f"{name}: {st[:4]}"
     # the quantizer's codes (8 bytes) and scales (1 byte) per block

@@ -46,6 +46,33 @@ def test_kv_write_read_float32_exact(rows, cols, s):
     assert np.array_equal(W.bf16_to_f32_numpy(out16).astype(np.float64), O.kv_fp8_dequantize(q, s, "bf16"))
 
 
+@pytest.mark.parametrize("s", [1.0, 0.0625, 0.37109375, 3.3e-3])
+@pytest.mark.parametrize("layout", ["contiguous", "strided"])
+def test_kv_write_in_range_ties(s, layout):
+    """Ties, their neighbours and grid values with no saturating element, so
+    whole wavefronts take the write's unclamped bracket; contiguous rows run
+    the linear-index kernel, strided rows the (row, chunk) walk."""
+    say(f"kv fp8 in-range ties s={s} {layout}")
+    rng = np.random.default_rng(17)
+    rows, cols = 96, 1024
+    mids = (O.E4M3_VALUES[1:] + O.E4M3_VALUES[:-1]) / 2
+    pool = np.concatenate([mids * s, O.E4M3_VALUES * s, [0.0, -0.0]]).astype(np.float32)
+    pool = np.concatenate([pool, np.nextafter(pool, np.float32(np.inf)), np.nextafter(pool, np.float32(-np.inf))])
+    pool = pool[np.abs(pool.astype(np.float64)) / np.float64(np.float32(s)) < 447.0]
+    x = (rng.choice(pool, size=(rows, cols)) * rng.choice([-1.0, 1.0], size=(rows, cols))).astype(np.float32)
+    xd = torch.from_numpy(x).to(DEV)
+    if layout == "strided":
+        wide = torch.zeros((rows, cols + 64), dtype=torch.float32, device=DEV)
+        wide[:, :cols] = xd
+        xd = wide[:, :cols]
+    sc = torch.tensor([s], dtype=torch.float32, device=DEV)
+    cache = nv.kv_fp8_quantize(xd, sc)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    bad = np.argwhere(got != O.kv_fp8_quantize(x, s))
+    assert bad.size == 0, f"{len(bad)} bytes differ, first {bad[:3].tolist()}"
+
+
 @pytest.mark.parametrize("s", [1e-40, 2.0 ** -126, 2.0 ** -120, 3.0e30])
 def test_kv_write_extreme_scales(s):
     """Subnormal, smallest-normal and huge scales (the write's estimate of
