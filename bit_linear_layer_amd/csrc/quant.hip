@@ -97,6 +97,27 @@ __global__ __launch_bounds__(kElemThreads) void amax_kernel(const uint8_t* __res
                                                             float* __restrict__ partials) {
   constexpr int kBlockBytes = DT == NVFP4_DTYPE_BF16 ? 32 : 64;
   float m = 0.0f;
+  // Contiguous rows: one linear block index, two blocks per iteration (both
+  // loads in flight together), no 64-bit row products.
+  if (ld_bytes == bpr * kBlockBytes) {
+    const int64_t total = rows * bpr, T = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < total; b += 2 * T) {
+      const bool ok1 = b + T < total;
+      RawBlock<DT> b0, b1;
+      b0.load(x + b * kBlockBytes);
+      b1.load(x + (ok1 ? b + T : b) * kBlockBytes);
+      float v[16];
+      b0.to_float(v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+      b1.to_float(v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+    m = block_max(m);
+    if (threadIdx.x == 0) partials[blockIdx.x] = m;
+    return;
+  }
   for (BlockWalk it(rows, bpr); it.valid(); it.next()) {
     RawBlock<DT> b;
     b.load(x + it.r * ld_bytes + it.j * kBlockBytes);
@@ -147,6 +168,32 @@ __global__ __launch_bounds__(kElemThreads) void quantize_kernel(
   // stores, so waiting for a load never waits for earlier stores (loads and
   // stores share one counter).  Past the end the load re-reads the current
   // block (a valid address) rather than branching around it.
+  // Contiguous x, codes and scales: the same pipelined loop over one linear
+  // block index (no 64-bit row products; h of the MLP step 68.7 -> 66.4 us,
+  // X 36 -> 34.7 us with its amax pass, same-process A/B).
+  if (ld_bytes == bpr * kBlockBytes && ld_codes == bpr * 8 && ld_scales == bpr) {
+    const int64_t total = rows * bpr, T = (int64_t)gridDim.x * blockDim.x;
+    int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= total) return;
+    RawBlock<DT> cur;
+    cur.load(x + b * kBlockBytes);
+    while (true) {
+      const int64_t bn = b + T;
+      const bool more = bn < total;
+      RawBlock<DT> nb;
+      nb.load(x + (more ? bn : b) * kBlockBytes);
+      float v[16];
+      cur.to_float(v);
+      uint2 c;
+      const uint32_t s = dev::quantize_block16(v, g, &c);
+      dev::store_stream8(codes + b * 8, c.x, c.y);
+      dev::store_stream1(scales + b, (uint8_t)s);
+      if (!more) break;
+      cur = nb;
+      b = bn;
+    }
+    return;
+  }
   BlockWalk it(rows, bpr);
   if (!it.valid()) return;
   RawBlock<DT> cur;
