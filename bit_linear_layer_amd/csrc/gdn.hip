@@ -22,7 +22,11 @@
 // kernel computes them for every (key head, chunk) in parallel, sharing k.k^T
 // and q.k^T among the value heads of a key head; a second walks
 // the chunks in order per (head, 32-row slice of S): the rows of S evolve
-// independently, so slices need no communication.
+// independently, so slices need no communication.  The normalized q and k
+// are stored once per key head and chunk, with the per-token factors G_t
+// and G_C / G_t per value head: the scan forms diag(G) Q and
+// (diag(G_C/G) K)^T itself with the same float32 products, so the workspace
+// written and read back is 44 % smaller.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,14 +49,24 @@ constexpr int kScanThreads = 512;   // scan workgroup
 constexpr int kP = kD + 4;   // rows of 128 floats
 constexpr int kPA = kC + 4;  // rows of 64 floats
 
-// Workspace per (value head, chunk), floats.
+// Workspace, floats: per (value head, chunk) a block of kWsPerChunk, all
+// value heads first; after them per (key head, chunk) a block of
+// kWsPerKeyChunk (room is reserved for as many key heads as value heads, so
+// the size depends on tokens and value heads only).
 constexpr int64_t kWsW = 0;                  // Wt   [64][128]
 constexpr int64_t kWsU = kWsW + kC * kD;     // Ut   [64][128]
 constexpr int64_t kWsA = kWsU + kC * kD;     // A    [64][64]
-constexpr int64_t kWsQ = kWsA + kC * kC;     // diag(G) Q        [64][128]
-constexpr int64_t kWsK = kWsQ + kC * kD;     // (diag(G_C / G) K)^T  [128][64]
-constexpr int64_t kWsG = kWsK + kC * kD;     // G_C (one float, padded to 4)
+constexpr int64_t kWsEG = kWsA + kC * kC;    // G_t = exp(cumulative log decay)  [64]
+constexpr int64_t kWsEC = kWsEG + kC;        // G_C / G_t  [64]
+constexpr int64_t kWsG = kWsEC + kC;         // G_C (one float, padded to 4)
 constexpr int64_t kWsPerChunk = kWsG + 4;
+constexpr int64_t kWsQN = 0;                 // normalized (and 128^-1/2-scaled) q  [64][128]
+constexpr int64_t kWsKT = kWsQN + kC * kD;   // normalized k, transposed  [128][64]
+constexpr int64_t kWsPerKeyChunk = kWsKT + kC * kD;
+
+__host__ __device__ inline int64_t key_block(int64_t hv, int64_t n_chunks, int64_t hk, int64_t chunk) {
+  return hv * n_chunks * kWsPerChunk + (hk * n_chunks + chunk) * kWsPerKeyChunk;
+}
 
 template <int DT>
 __device__ inline float load_elem(const void* base, int64_t idx) {
@@ -172,6 +186,21 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
     }
   }
   __syncthreads();
+  {
+    // the normalized q rows and k^T (key dimension major: the scan reads it
+    // down the token axis) of this key head and chunk
+    float* kout = ws + key_block(p.hv, p.n_chunks, hk, chunk);
+#pragma unroll
+    for (int e = 0; e < 16; e += 4)
+      *reinterpret_cast<floatx4*>(kout + kWsQN + rt * kD + part * 16 + e) =
+          *reinterpret_cast<const floatx4*>(&sq[rt][part * 16 + e]);
+    const int d = tid >> 2, tq = (tid & 3) * 16;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const int t = tq + e;
+      *reinterpret_cast<floatx4*>(kout + kWsKT + d * kC + t) = floatx4{sk[t][d], sk[t + 1][d], sk[t + 2][d], sk[t + 3][d]};
+    }
+  }
 
   // K K^T (waves 0-3) or Q K^T (waves 4-7), rows 16 rb.., all 64 columns:
   // gram[cb][r] = (X K^T)[16 rb + 4 lg + r][16 cb + li]
@@ -205,10 +234,13 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
       const bool ok = t0 + lane < p.T;  // tokens past T: beta = 0, g = 0
       const float b = ok ? bn : 0.0f;
       const float gam = wave_prefix_sum(ok ? gn : 0.0f, lane);
+      const float eg = expf(gam), ec = expf(__shfl(gam, 63) - gam);
       sbeta[lane] = b;
       sgam[lane] = gam;
-      scw[lane] = b * expf(gam);
-      segc[lane] = expf(__shfl(gam, 63) - gam);
+      scw[lane] = b * eg;
+      segc[lane] = ec;
+      out[kWsEG + lane] = eg;
+      out[kWsEC + lane] = ec;
     }
     __syncthreads();
     // the next head's operands (the last head reloads itself) ahead of this
@@ -230,26 +262,7 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
           out[kWsA + t * kC + j] = j <= t ? dec * gram[cb][r] : 0.0f;
       }
     }
-    // diag(G) Q, (diag(G_C / G) K)^T (key dimension major: the scan reads it
-    // down the token axis), G_C
-    const float gc = sgam[kC - 1];
-    {
-      const float eg = expf(sgam[rt]);
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const floatx4 qv = *reinterpret_cast<const floatx4*>(&sq[rt][part * 16 + e]);
-        *reinterpret_cast<floatx4*>(out + kWsQ + rt * kD + part * 16 + e) = qv * eg;
-      }
-      const int d = tid >> 2, tq = (tid & 3) * 16;
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        const int t = tq + e;
-        *reinterpret_cast<floatx4*>(out + kWsK + d * kC + t) =
-            floatx4{segc[t] * sk[t][d], segc[t + 1] * sk[t + 1][d], segc[t + 2] * sk[t + 2][d],
-                    segc[t + 3] * sk[t + 3][d]};
-      }
-    }
-    if (tid == 0) out[kWsG] = expf(gc);
+    if (tid == 0) out[kWsG] = expf(sgam[kC - 1]);  // G_C
     __syncthreads();  // M complete
 
     // diagonal blocks of T: lane (block i, column c) solves (I + M_ii) x = e_c
@@ -341,18 +354,26 @@ __global__ __launch_bounds__(kPrepThreads) void gdn_prep_kernel(GdnArgs p, float
 // lane's Ut elements and G_C (read by the second).  Thread tid holds 4-float
 // groups tid + 512 i of each array.  Native vector types: arrays of HIP's
 // float4 class stay in scratch memory.
-__device__ __attribute__((always_inline)) inline void scan_load_wq(const float* in, int tid, floatx4 (&w)[4],
-                                                                     floatx4 (&q)[4]) {
+__device__ __attribute__((always_inline)) inline void scan_load_wq(const float* in, const float* kin, int tid,
+                                                                     floatx4 (&w)[4], floatx4 (&q)[4],
+                                                                     float (&eg)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    w[i] = reinterpret_cast<const floatx4*>(in + kWsW)[tid + i * kScanThreads];
-    q[i] = reinterpret_cast<const floatx4*>(in + kWsQ)[tid + i * kScanThreads];
+    const int f = tid + i * kScanThreads;
+    w[i] = reinterpret_cast<const floatx4*>(in + kWsW)[f];
+    q[i] = reinterpret_cast<const floatx4*>(kin + kWsQN)[f];
+    eg[i] = in[kWsEG + f / (kD / 4)];  // the row (token) of q's group
   }
 }
-__device__ __attribute__((always_inline)) inline void scan_load_ka(const float* in, int tid, int uoff, floatx4 (&k)[4],
+__device__ __attribute__((always_inline)) inline void scan_load_ka(const float* in, const float* kin, int tid, int uoff,
+                                                                     floatx4 (&k)[4], floatx4 (&ec)[4],
                                                                      floatx4 (&a)[2], float (&u)[4], float& gc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) k[i] = reinterpret_cast<const floatx4*>(in + kWsK)[tid + i * kScanThreads];
+  for (int i = 0; i < 4; ++i) {
+    const int f = tid + i * kScanThreads;
+    k[i] = reinterpret_cast<const floatx4*>(kin + kWsKT)[f];
+    ec[i] = *reinterpret_cast<const floatx4*>(in + kWsEC + (f % (kC / 4)) * 4);  // the group's 4 tokens
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) a[i] = reinterpret_cast<const floatx4*>(in + kWsA)[tid + i * kScanThreads];
 #pragma unroll
@@ -382,11 +403,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   const int ti = wave >> 1, tj = wave & 1;  // U / O tile
   const int row0 = sl * kSlice;
   const float* base = ws + (int64_t)h * p.n_chunks * kWsPerChunk;
+  const float* kbase = ws + key_block(p.hv, p.n_chunks, h / (p.hv / p.hk), 0);
   const int last = p.n_chunks - 1;
 
   const int uoff = (16 * ti + 4 * lk) * kD + row0 + 16 * tj + li;  // this lane's Ut elements
-  floatx4 nw[4], nq[4], nk[4], na[2];
-  float nu[4], ngc;
+  floatx4 nw[4], nq[4], nk[4], nec[4], na[2];
+  float neg[4], nu[4], ngc;
 
   auto put_wq = [&]() {  // Wt, diag(G) Q registers -> LDS
 #pragma unroll
@@ -394,14 +416,14 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
       const int f = tid + i * kScanThreads;
       const int rr = f / (kD / 4), cc = (f % (kD / 4)) * 4;
       *reinterpret_cast<floatx4*>(&sW[rr][cc]) = nw[i];
-      *reinterpret_cast<floatx4*>(&sQ[rr][cc]) = nq[i];
+      *reinterpret_cast<floatx4*>(&sQ[rr][cc]) = nq[i] * neg[i];
     }
   };
-  auto put_ka = [&]() {  // K^T, A registers -> LDS
+  auto put_ka = [&]() {  // (diag(G_C/G) K)^T, A registers -> LDS
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int f = tid + i * kScanThreads;
-      *reinterpret_cast<floatx4*>(&sKT[f / (kC / 4)][(f % (kC / 4)) * 4]) = nk[i];
+      *reinterpret_cast<floatx4*>(&sKT[f / (kC / 4)][(f % (kC / 4)) * 4]) = nk[i] * nec[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -414,8 +436,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
     const int c = i / kD, d = i % kD;
     sS[c][d] = p.s0 != nullptr ? p.s0[((int64_t)h * kD + row0 + c) * kD + d] : 0.0f;
   }
-  scan_load_wq(base, tid, nw, nq);
-  scan_load_ka(base, tid, uoff, nk, na, nu, ngc);
+  scan_load_wq(base, kbase, tid, nw, nq, neg);
+  scan_load_ka(base, kbase, tid, uoff, nk, nec, na, nu, ngc);
   put_wq();
   __syncthreads();
 
@@ -427,8 +449,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   // makes the compiler wait for it where the paths join.
   for (int chunk = 0; chunk < p.n_chunks; ++chunk) {
     const float* nxt = base + (int64_t)min(chunk + 1, last) * kWsPerChunk;
+    const float* knxt = kbase + (int64_t)min(chunk + 1, last) * kWsPerKeyChunk;
     // ---- phase 1
-    scan_load_wq(nxt, tid, nw, nq);
+    scan_load_wq(nxt, knxt, tid, nw, nq, neg);
     // P = Wt S^T and O = diag(G) Q S^T on this wave's tile; inside each
     // 16-wide K block the lane group lk takes k = 4 lk + s at step s (any
     // order of k gives the same sum), so each operand is one 16-byte read
@@ -450,7 +473,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
     __syncthreads();  // U, K^T, A of this chunk in LDS; every read of Wt, Q, S done
     // ---- phase 2
     const float gc = ngc;
-    scan_load_ka(nxt, tid, uoff, nk, na, nu, ngc);
+    scan_load_ka(nxt, knxt, tid, uoff, nk, nec, na, nu, ngc);
     // O += A U over key blocks kb <= ti (A is lower triangular)
     for (int kb = 0; kb <= ti; ++kb) {
       const floatx4 aa = *reinterpret_cast<const floatx4*>(&sA[16 * ti + li][16 * kb + 4 * lk]);
@@ -500,7 +523,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
 
 size_t gdn_workspace_floats(int64_t T, int hv) {
   const int64_t chunks = (T + kC - 1) / kC;
-  return (size_t)(chunks * hv * kWsPerChunk);
+  return (size_t)(chunks * hv * (kWsPerChunk + kWsPerKeyChunk));
 }
 
 hipError_t launch_gdn(const GdnArgs& p, float* ws, hipStream_t s) {
