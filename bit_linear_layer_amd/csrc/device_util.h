@@ -69,22 +69,25 @@ __device__ inline void store_stream8(void* p, uint32_t a, uint32_t b) {
 }
 __device__ inline void store_stream1(uint8_t* p, uint8_t v) { __builtin_nontemporal_store(v, p); }
 
-// E4M3 byte -> fp16 pair (s, s), exact: the byte shifted into an fp16's
-// exponent/mantissa fields is s * 2^-8 (normal and subnormal alike).
+// E4M3 byte b -> the fp16 pair (s * 2^-8, s * 2^-8), exact: b shifted into
+// an fp16's exponent/mantissa fields is s * 2^-8 (normal and subnormal
+// alike).  decode8 converts the codes with a 2^8 scale, so the product is
+// code * s with no separate correction.
 __device__ inline half2v scale_pair(uint32_t sdw, int idx) {
   const uint32_t b = (sdw >> (8 * idx)) & 0xFFu;
-  const uint32_t bits = (b << 7) | (b << 23);
-  half2v h = __builtin_bit_cast(half2v, bits);
-  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
-  return h * k256;
+  return __builtin_bit_cast(half2v, (b << 7) | (b << 23));
 }
 
-// 8 E2M1 codes (one dword) times their block scale -> 8 exact fp16 values.
+// 8 E2M1 codes (one dword) times their block scale -> 8 exact fp16 values:
+// the conversion applies the exponent of its float32 scale operand, so the
+// codes come out times 2^8 (at most 1536, exact), and one fp16 multiply by
+// s * 2^-8 from scale_pair gives code * s (<= 5 significant bits, at least
+// 2^-10: exact and normal).
 __device__ inline half8 decode8(uint32_t codes, half2v s2) {
-  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
-  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
-  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
-  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3);
   p0 *= s2;
   p1 *= s2;
   p2 *= s2;
