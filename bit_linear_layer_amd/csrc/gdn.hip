@@ -26,7 +26,7 @@
 // are stored once per key head and chunk, with the per-token factors G_t
 // and G_C / G_t per value head: the scan forms diag(G) Q and
 // (diag(G_C/G) K)^T itself with the same float32 products, so the workspace
-// written and read back is 44 % smaller.
+// written and read back is 29 % smaller (44 % per value head).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
