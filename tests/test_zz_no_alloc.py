@@ -3,7 +3,8 @@ the library's static per-GPU scratch array) against nvfp4_quantize with a
 caller workspace, through the C ABI: codes, scales and global scale bit for
 bit, on consecutive calls whose sizes shrink and grow again (the scratch
 keeps the previous call's contents), dynamic and static, bf16 and float32,
-the one-launch small path and the two-launch path; plus the oracle."""
+the one-launch small path and the two-launch path; plus the oracle; and
+the call captured in a HIP graph and replayed."""
 import numpy as np
 import pytest
 import torch
@@ -66,3 +67,31 @@ def test_noalloc_rejects_precomputed_amax():
     q = nv.empty_nvfp4(4, 32, DEV)
     with pytest.raises(nv.NVFP4Error):
         nv.nvfp4_quantize_noalloc(x, q, nv.AMAX_PRECOMPUTED)
+
+
+def test_noalloc_replayed_from_a_hip_graph():
+    """What the entry point is for: a call captured in a HIP graph (nothing
+    allocates inside the capture), replayed four times on new inputs with
+    eager calls of the same entry point in between (they share the scratch
+    array, in stream order); every replay bit for bit nvfp4_quantize's
+    result with a workspace."""
+    r, c = 700, 5120
+    x = x_of(r, c, 300, torch.bfloat16)
+    q = nv.empty_nvfp4(r, c, DEV)
+    nv.nvfp4_quantize_noalloc(x, q)  # outside the capture: the scratch address lookup
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.nvfp4_quantize_noalloc(x, q)
+    ws = nv.workspace_for(r, c, DEV)
+    for i in range(4):
+        say(f"quantize_noalloc graph replay {i}")
+        x.copy_(x_of(r, c, 301 + i, torch.bfloat16))
+        both(x_of(64, 256, 400 + i, torch.bfloat16))  # eager use of the same scratch in between
+        q.codes.fill_(0xAB)
+        graph.replay()
+        q_ref = nv.empty_nvfp4(r, c, DEV)
+        nv.nvfp4_quantize(x, q_ref, nv.SCALE_DYNAMIC, ws)
+        a, b = host_q(q_ref), host_q(q)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        assert a[2].view(np.uint32) == b[2].view(np.uint32)
