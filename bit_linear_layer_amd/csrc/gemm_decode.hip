@@ -45,10 +45,10 @@ using namespace dev;
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSlices = 8;  // K slices of a 16-row group (units of the packed layout)
-// groups per round: one 16x16 partial each in registers (fewer for wide
-// K slices, whose activations take more registers)
-template <int Q>
-constexpr int round_of() { return Q >= 6 ? 8 : 16; }
+// groups per round: one 16x16 partial each in LDS (fewer for wide K slices,
+// whose activations take more registers), a whole number of D-unit steps
+template <int Q, int D>
+constexpr int round_of() { return (Q >= 6 ? 8 : 16) / D * D; }
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -333,7 +333,7 @@ void decode_kernel(const DecodeArgs p, int groups) {
   // use (an invalid group loads nothing and writes its partial to a spare
   // LDS slot), so the waits stay exact: each step waits only for the unit
   // it computes, the next D - 1 units stay in flight.
-  constexpr int kRound = round_of<Q>();
+  constexpr int kRound = round_of<Q, D>();
   static_assert(kRound % D == 0, "every round starts on buffer 0");
   floatx4* red = reinterpret_cast<floatx4*>(smem);  // [kRound + 1][8 waves][64 lanes]
   barrier_lds();  // every wave has read its activations from the LDS staging
@@ -460,7 +460,7 @@ hipError_t launch_q(const DecodeArgs& p, bool gate, hipStream_t s) {
   const int grid = groups < cus ? groups : cus;
   const int xq = p.x == nullptr ? 0 : (p.x_dtype == NVFP4_DTYPE_BF16 ? 1 : 2);
   constexpr int NW = kSlices / S;
-  size_t lds = (size_t)(round_of<Q>() + 1) * NW * 64 * 16;
+  size_t lds = (size_t)(round_of<Q, D>() + 1) * NW * 64 * 16;
   if (xq != 0) {
     const size_t a = (size_t)p.M * (lds_code_stride(p.K) + lds_scale_stride(p.K));
     if (a > lds) lds = a;
@@ -534,7 +534,7 @@ hipError_t launch_gemm_decode(const GemmArgs& g, const uint8_t* packed, const vo
     case 2: return launch_q<2, 4, 1>(p, gate, s);
     case 3: return launch_q<3, 2, 1>(p, gate, s);
     case 4: return launch_q<4, 2, 1>(p, gate, s);
-    case 5: return launch_q<5, 2, 1>(p, gate, s);
+    case 5: return launch_q<5, 3, 1>(p, gate, s);  // K = 5120: three units in flight (2: 0.7-1.3 us slower, 4: slower)
     case 6: return launch_q<6, 2, 1>(p, gate, s);
     case 7: return launch_q<7, 2, 1>(p, gate, s);
     case 8: return launch_q<8, 1, 1>(p, gate, s);
