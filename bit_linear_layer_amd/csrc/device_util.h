@@ -55,10 +55,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Streaming stores, for results that the same launch never reads back: the
 // nontemporal hint (global_store ... nt) keeps them from displacing inputs
 // that are still being re-read through the caches.  Measured on one MI355X:
-// FP8 KV-cache write of 32768 x 1024 bf16 21.7 -> 16.8 us, NVFP4 quantization
-// of the 8192 x 17408 MLP activation 77 -> 66 us, bf16 GEMM outputs about
-// 1 %.  The hint is IR metadata that a rewrite of the store can lose, so the
-// build tests look for the nt stores in the code objects.
+// NVFP4 quantization of the 8192 x 17408 MLP activation 77 -> 66 us, bf16
+// GEMM outputs about 1 %, FP8 KV-cache write of 32768 x 1024 bf16 21.7 ->
+// 20.0 us (16 rotating buffers, so no input is left in the last-level
+// cache).  The hint is IR metadata that a rewrite of the store can lose, so
+// the build tests look for the nt stores in the code objects.
 __device__ inline void store_stream16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const u32x4 v = {a, b, c, d};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));

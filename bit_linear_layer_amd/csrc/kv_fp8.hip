@@ -85,11 +85,12 @@ struct ChunkWalk {
 // cache and output bytes go out as streaming stores.  A write of contiguous
 // rows without slots runs a kernel that walks one linear chunk index
 // instead of (row, chunk) pairs and 64-bit row products, and issues both
-// loads before the first wait.  Measured on 32768 x 1024 bf16 against one
-// chunk per iteration with plain stores: unit-scale write 21.7 -> 16.8 us,
-// calibrated write 25.7 -> 19.2 us (the linear walk and the skipped clamps
-// -3.4 us of it), bf16 read 20.3 -> 16.6 us; four chunks per iteration, or
-// fewer workgroups, were slower.
+// loads before the first wait.  Measured on 32768 x 1024 bf16 with 16
+// rotating buffers (none left in the last-level cache), against one chunk
+// per iteration with plain stores: calibrated write 25.7 -> 21.4 us (the
+// linear walk and the skipped clamps -2.9 us of it), unit-scale write
+// 21.7 -> 20.3 us, bf16 read unchanged at 20.5-20.9 us; four chunks per
+// iteration, or fewer workgroups, were slower.
 constexpr int kChunksPerIter = 2;
 
 // Magnitude of the E4M3 byte P of `src`, decoded by the hardware conversion (exact).
