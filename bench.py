@@ -382,6 +382,9 @@ def kv_fp8(nv, W, torch, dev, stream, log):
     rate("kv_fp8_write_unit_scale", lambda: (lambda i: nv.nvfp4_kv_fp8_quantize(xs[i], caches[i], s_one))(nxt()), 3 * n)
     rate("kv_fp8_read_bf16", lambda: (lambda i: nv.nvfp4_kv_fp8_dequantize(caches[i], s_cal, outs[i]))(nxt()), 3 * n)
     rate("kv_fp8_calibrate", lambda: (lambda i: nv.nvfp4_kv_fp8_calibrate(xs[i], s_cal, ws))(nxt()), 2 * n)
+    # context, not a kernel of this library: a plain device copy of the
+    # same rotating bf16 tensors (2 B read + 2 B written per element)
+    rate("context_torch_copy_bf16", lambda: (lambda i: outs[i].copy_(xs[i]))(nxt()), 4 * n)
     for k, v in res.items():
         log(f"{k}: {v['us']} us = {v['GBps']} GB/s")
     return {"kv_fp8_cache": {"workload": wl.name, "algorithmic_bytes_per_element": "write 3, read 3, calibrate 2",
