@@ -478,6 +478,10 @@ def decode(nv, W, torch, dev, stream, log):
     t_row = timed(lambda i: nv.nvfp4_gemm_fused_segments(ad, rowmajor[i % ROTATE], offs, g, outd))
     t_row_q = timed(lambda i: (nv.nvfp4_quantize(xd, ad, nv.SCALE_DYNAMIC, wsd),
                                nv.nvfp4_gemm_fused_segments(ad, rowmajor[i % ROTATE], offs, g, outd)))
+    # context, not a kernel of this library: torch reading the same rotating
+    # 100 MB weight copies once (a max-reduction over their bytes)
+    flat = [p.data.view(torch.int32) for p in packed]
+    t_ctx = timed(lambda i: torch.amax(flat[i % ROTATE]))
     m = xd.shape[0]
     alg_bytes = rows * kk // 2 + rows * kk // 16 + m * kk // 2 + m * kk // 16 + m * rows * 2
     alg_full = rows * kk // 2 + rows * kk // 16 + m * kk * 2 + m * rows * 2
@@ -492,11 +496,13 @@ def decode(nv, W, torch, dev, stream, log):
                         "quantize_plus_gemm_us": round(t_full * 1e6, 2),
                         "quantize_plus_gemm_frac_of_hbm_peak": round(alg_full / t_full / 1e9 / HBM_PEAK_GBS, 4),
                         "quantize_plus_gemm_path": "nvfp4_linear_decode (activations quantized in the launch)",
-                        "rowmajor_quantize_plus_gemm_us": round(t_row_q * 1e6, 2)}
+                        "rowmajor_quantize_plus_gemm_us": round(t_row_q * 1e6, 2),
+                        "context_torch_read_weight_us": round(t_ctx * 1e6, 2),
+                        "context_torch_read_weight_GBps": round(flat[0].numel() * 4 / t_ctx / 1e9, 1)}
     log(f"decode: gemm {best * 1e6:.1f} us = {alg_bytes / best / 1e9:.0f} GB/s (row-major {t_row * 1e6:.1f}, decode "
         f"layout {t_gemm * 1e6:.1f} us); linear layer with in-launch quantization {t_full * 1e6:.1f} us; "
-        f"row-major quantize + gemm {t_row_q * 1e6:.1f} us")
-    del packed, rowmajor, base, outd
+        f"row-major quantize + gemm {t_row_q * 1e6:.1f} us; torch reading the weight once {t_ctx * 1e6:.1f} us")
+    del packed, rowmajor, base, outd, flat
     return res
 
 
