@@ -562,7 +562,8 @@ def gdn_study(nv, W, torch, stream, log, dev):
     activations, float32 products) in-projection, along the sequence; and the
     erasure of a state impulse (10 % of |S|) injected at token 8192, in steps
     until it falls below 1/e and 10 %, beside each head's pure-decay horizon
-    1 / mean(-g)."""
+    1 / mean(-g), the keys' effective rank, and the same erasure with the
+    keys replaced by isotropic random directions."""
     gw = W.gdn_layer()
     xg = gw.x.to(dev)
     T = xg.shape[0]
@@ -621,33 +622,64 @@ def gdn_study(nv, W, torch, stream, log, dev):
             for m, r in zip(marks, rel)}
     log("relS mean: " + ", ".join(f"{m}:{v['mean']:.3f}" for m, v in rels.items()))
 
-    # impulse erasure on the reference dynamics
+    # impulse erasure: a state impulse of 10 % of |S| injected at token
+    # 8192, followed against the unperturbed run
     t0 = 8192
-    s_t0 = states(ref, [t0])[0]
-    gen = torch.Generator(device=dev).manual_seed(0)
-    imp = torch.randn(s_t0.shape, device=dev, generator=gen)
-    imp *= (0.1 * s_t0.flatten(1).norm(dim=1) / imp.flatten(1).norm(dim=1))[:, None, None]
     ends = list(range(t0 + 16, t0 + 1025, 16)) + list(range(t0 + 1152, min(T, t0 + 8192) + 1, 128))
-    base = states(ref, ends, s_init=s_t0, t_begin=t0)
-    pert = states(ref, ends, s_init=s_t0 + imp, t_begin=t0)
-    norm0 = imp.flatten(1).norm(dim=1)
-    ratio = torch.stack([(p_ - b_).flatten(1).norm(dim=1) / norm0 for p_, b_ in zip(pert, base)])  # [steps, hv]
     steps = torch.tensor([e - t0 for e in ends], device=dev, dtype=torch.float32)
 
-    def first_below(th):
-        below = ratio < th
-        idx = torch.where(below.any(dim=0), below.float().argmax(dim=0), torch.full((hv,), len(ends) - 1, device=dev))
-        return steps[idx]
-    e1, e10 = first_below(float(torch.exp(torch.tensor(-1.0)))), first_below(0.1)
+    def erasure(src, seed):
+        s_t0 = states(src, [t0])[0]
+        gen = torch.Generator(device=dev).manual_seed(seed)
+        imp = torch.randn(s_t0.shape, device=dev, generator=gen)
+        imp *= (0.1 * s_t0.flatten(1).norm(dim=1) / imp.flatten(1).norm(dim=1))[:, None, None]
+        base = states(src, ends, s_init=s_t0, t_begin=t0)
+        pert = states(src, ends, s_init=s_t0 + imp, t_begin=t0)
+        norm0 = imp.flatten(1).norm(dim=1)
+        ratio = torch.stack([(p_ - b_).flatten(1).norm(dim=1) / norm0 for p_, b_ in zip(pert, base)])  # [steps, hv]
+
+        def first_below(th):
+            below = ratio < th
+            idx = torch.where(below.any(dim=0), below.float().argmax(dim=0), torch.full((hv,), len(ends) - 1, device=dev))
+            return steps[idx]
+        e1, e10 = first_below(float(torch.exp(torch.tensor(-1.0)))), first_below(0.1)
+        return ({"median": e1.median().item(), "min": e1.min().item(), "max": e1.max().item()},
+                {"median": e10.median().item(), "min": e10.min().item(), "max": e10.max().item()})
+
+    def key_effective_rank(src):
+        """Participation ratio (tr C)^2 / tr(C^2) of the unit keys' second
+        moment C per key head: 128 for isotropic keys, r for keys spread
+        evenly over r directions."""
+        kn = cols(src, 1).reshape(T, hk, 128).permute(1, 0, 2)
+        kn = kn / kn.norm(dim=2, keepdim=True).clamp_min(1e-30)
+        c = torch.matmul(kn.transpose(1, 2).contiguous(), kn) / T  # [hk, 128, 128]
+        pr = c.diagonal(dim1=1, dim2=2).sum(dim=1) ** 2 / (c * c).sum(dim=(1, 2))
+        return {"median": round(pr.median().item(), 1), "min": round(pr.min().item(), 1),
+                "max": round(pr.max().item(), 1)}
+
+    e1, e10 = erasure(ref, 0)
     horizon = 1.0 / (-ref[:, a0:offs[6]].mean(dim=0))
-    imp_res = {"steps_to_1_over_e": {"median": e1.median().item(), "min": e1.min().item(), "max": e1.max().item()},
-               "steps_to_10pct": {"median": e10.median().item(), "min": e10.min().item(), "max": e10.max().item()},
+    rank_layer = key_effective_rank(ref)
+    # the same dynamics (beta, g, q, v) with the keys replaced by isotropic
+    # random directions: how much of the erasure time the keys' spread sets
+    iso = ref.clone()
+    gen = torch.Generator(device=dev).manual_seed(1)
+    iso[:, offs[1]:offs[2]] = torch.randn((T, offs[2] - offs[1]), device=dev, generator=gen)
+    rank_iso = key_effective_rank(iso)
+    e1_iso, e10_iso = erasure(iso, 0)
+    del iso
+    imp_res = {"steps_to_1_over_e": e1, "steps_to_10pct": e10,
                "pure_decay_horizon_tokens": {"median": round(horizon.median().item(), 1),
                                              "min": round(horizon.min().item(), 1),
                                              "max": round(horizon.max().item(), 1)},
+               "key_effective_rank": rank_layer,
+               "isotropic_keys": {"steps_to_1_over_e": e1_iso, "steps_to_10pct": e10_iso,
+                                  "key_effective_rank": rank_iso},
                "resolution_tokens": "16 up to 1024 steps, then 128"}
-    log(f"impulse: 1/e after median {imp_res['steps_to_1_over_e']['median']:.0f} steps "
-        f"(pure-decay horizon median {imp_res['pure_decay_horizon_tokens']['median']:.0f} tokens)")
+    log(f"impulse: 1/e after median {e1['median']:.0f} steps "
+        f"(pure-decay horizon median {imp_res['pure_decay_horizon_tokens']['median']:.0f} tokens); "
+        f"keys' effective rank median {rank_layer['median']}; isotropic keys (rank {rank_iso['median']}): "
+        f"1/e after median {e1_iso['median']:.0f} steps")
     del ref, outq
     return {"ms": round(ms, 3), "tflops_fp32": round(flops / (ms * 1e-3) / 1e12, 2),
             "algorithmic_flops": flops, "relS_vs_unquantized": rels, "impulse_erasure": imp_res,
