@@ -396,7 +396,7 @@ typedef struct {
 } nvfp4_gdn_inputs;
 
 /* Bytes of device workspace nvfp4_gdn_recurrence needs (per-chunk data,
- * about 148 KB per value head and 64 tokens). */
+ * about 115 KB per value head and 64 tokens). */
 size_t nvfp4_gdn_workspace_bytes(int64_t tokens, int v_heads);
 
 /*

@@ -30,7 +30,7 @@ int partial_count(int64_t rows, int64_t cols, int chunk) {
   if (wg > kMaxPartials) wg = kMaxPartials;
   return (int)wg;
 }
-size_t gdn_workspace_floats(int64_t T, int hv) { return (size_t)((T + 63) / 64) * hv * (20612 + 16384); }
+size_t gdn_workspace_floats(int64_t T, int hv) { return (size_t)((T + 63) / 64) * hv * (12420 + 16384); }
 size_t decode_weight_bytes(int64_t N, int64_t K) { return (size_t)((N + 15) / 16) * 8 * ((K + 1023) / 1024) * 1152; }
 
 hipError_t launch_amax(const void*, int, int64_t, int64_t, int64_t, float*, int, hipStream_t) { return record(); }
