@@ -44,7 +44,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;   // head dimension (keys and values)
 constexpr int kC = 64;    // tokens per chunk
 constexpr int kSlice = 32;  // state rows per scan workgroup
-constexpr int kScanThreads = 512;   // scan workgroup
+constexpr int kScanThreads = 1024;  // scan workgroup: 16 waves
 // LDS row strides, padded so the 16 rows a wave reads at once fall into
 // distinct banks (an unpadded 512-byte stride puts them all in one)
 constexpr int kP = kD + 4;   // rows of 128 floats
@@ -380,29 +380,36 @@ void gdn_prep_kernel(GdnArgs p, float* __restrict__ ws) {
   }
 }
 
-// One workgroup per (value head, 32-row slice of S); chunks in order.  The
-// three products of a chunk run on v_mfma_f32_16x16x4f32 (fp32 in, fp32
-// accumulate; lane l supplies A[l%16][l/16] and B[l/16][l%16] and holds
-// D[4(l/16)+r][l%16]); inside each 16-wide K block lane group l/16 takes
-// k = 4(l/16) + s at step s, so operands are 16-byte LDS reads (R is kept
-// transposed, Z arrives transposed):
-//   wave w: Y = diag(G) K S^T and O = diag(G) Q S^T for the 16x16 tile
-//           (t: 16(w/2).., c: 16(w%2)..), R = diag(beta) (V - Y), then
-//           O += (A T) R;
-//   wave w: S[c][16w..16w+15] = G_C S + R^T Z for both 16-row halves of
-//           the slice.
+// One workgroup (16 waves) per (value head, 32-row slice of S); chunks in
+// order.  The three products of a chunk run on v_mfma_f32_16x16x4f32 (fp32
+// in, fp32 accumulate; lane l supplies A[l%16][l/16] and B[l/16][l%16] and
+// holds D[4(l/16)+r][l%16]); inside each 16-wide K block lane group l/16
+// takes k = 4(l/16) + s at step s, so operands are 16-byte LDS reads (R is
+// kept transposed, Z arrives transposed).  One 16x16 tile per wave and phase,
+// four waves per SIMD to cover each other's operand and barrier latency:
+//   phase 1, wave w: tile (t: 16 ti.., c: 16 tj..), ti = (w%8)/2, tj = w%2,
+//            of Y = diag(G) K S^T (w < 8; then R = diag(beta) (V - Y)) or
+//            of O = diag(G) Q S^T (w >= 8);
+//   phase 2, waves w >= 8: O += (A T) R, stored; every wave w: the state
+//            tile S[16 (w/8)..][16 (w%8)..] = G_C S + R^T Z.
 // The next chunk's data is loaded into registers while one is computed.
+
+constexpr int kKQGroups = kC * kD / 4 / kScanThreads;  // 4-float groups per thread of q, k rows
+constexpr int kZGroups = kD * kC / 4 / kScanThreads;   // of Z^T
+constexpr int kAGroups = kC * kC / 4 / kScanThreads;   // of A T
+static_assert(kKQGroups >= 1 && kZGroups >= 1 && kAGroups >= 1, "every thread loads whole groups");
 
 // A chunk's data in registers, in two halves loaded at different points:
 // the normalized k and q rows with G_t (read by the first phase of a step),
 // and Z^T, A T, the lane's value elements and beta_t, and G_C (read by the
-// second).  Thread tid holds 4-float groups tid + 512 i of each array.
-// Native vector types: arrays of HIP's float4 class stay in scratch memory.
+// second).  Thread tid holds 4-float groups tid + kScanThreads i of each
+// array.  Native vector types: arrays of HIP's float4 class stay in scratch
+// memory.
 __device__ __attribute__((always_inline)) inline void scan_load_kq(const float* in, const float* kin, int tid,
-                                                                     floatx4 (&k)[4], floatx4 (&q)[4],
-                                                                     float (&eg)[4]) {
+                                                                     floatx4 (&k)[kKQGroups], floatx4 (&q)[kKQGroups],
+                                                                     float (&eg)[kKQGroups]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kKQGroups; ++i) {
     const int f = tid + i * kScanThreads;
     k[i] = reinterpret_cast<const floatx4*>(kin + kWsKN)[f];
     q[i] = reinterpret_cast<const floatx4*>(kin + kWsQN)[f];
@@ -414,12 +421,12 @@ __device__ __attribute__((always_inline)) inline void scan_load_kq(const float* 
 template <int DT>
 __device__ __attribute__((always_inline)) inline void scan_load_za(const float* in, const GdnArgs& p, int tid,
                                                                      int boff, int64_t vrow, int64_t vcol,
-                                                                     floatx4 (&z)[4], floatx4 (&a)[2], float (&v)[4],
-                                                                     floatx4& beta, float& gc) {
+                                                                     floatx4 (&z)[kZGroups], floatx4 (&a)[kAGroups],
+                                                                     float (&v)[4], floatx4& beta, float& gc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) z[i] = reinterpret_cast<const floatx4*>(in + kWsZ)[tid + i * kScanThreads];
+  for (int i = 0; i < kZGroups; ++i) z[i] = reinterpret_cast<const floatx4*>(in + kWsZ)[tid + i * kScanThreads];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) a[i] = reinterpret_cast<const floatx4*>(in + kWsAT)[tid + i * kScanThreads];
+  for (int i = 0; i < kAGroups; ++i) a[i] = reinterpret_cast<const floatx4*>(in + kWsAT)[tid + i * kScanThreads];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int64_t row = vrow + r < p.T ? vrow + r : p.T - 1;
@@ -448,7 +455,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  const int ti = wave >> 1, tj = wave & 1;  // R / O tile
+  const bool oprod = wave >= 8;                          // phase 1: O tile (else Y tile)
+  const int ti = (wave & 7) >> 1, tj = wave & 1;         // the phase-1 tile
+  const int tc = wave >> 3, cbk = wave & 7;              // the phase-2 state tile
   const int row0 = sl * kSlice;
   const float* base = ws + (int64_t)h * p.n_chunks * kWsPerChunk;
   const float* kbase = ws + key_block(p.hv, p.n_chunks, h / (p.hv / p.hk), 0);
@@ -456,12 +465,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
 
   const int boff = 16 * ti + 4 * lk;                 // the lane's four tokens in a chunk
   const int64_t vcol = (int64_t)h * kD + row0 + 16 * tj + li;  // and its value column
-  floatx4 nk[4], nq[4], nz[4], na[2], nb;
-  float neg[4], nv[4], ngc;
+  floatx4 nk[kKQGroups], nq[kKQGroups], nz[kZGroups], na[kAGroups], nb;
+  float neg[kKQGroups], nv[4], ngc;
 
   auto put_kq = [&]() {  // diag(G) K, diag(G) Q registers -> LDS
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kKQGroups; ++i) {
       const int f = tid + i * kScanThreads;
       const int rr = f / (kD / 4), cc = (f % (kD / 4)) * 4;
       *reinterpret_cast<floatx4*>(&sK[rr][cc]) = nk[i] * neg[i];
@@ -470,12 +479,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
   };
   auto put_za = [&]() {  // Z^T, A T registers -> LDS
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kZGroups; ++i) {
       const int f = tid + i * kScanThreads;
       *reinterpret_cast<floatx4*>(&sZT[f / (kC / 4)][(f % (kC / 4)) * 4]) = nz[i];
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kAGroups; ++i) {
       const int f = tid + i * kScanThreads;
       *reinterpret_cast<floatx4*>(&sA[f / (kC / 4)][(f % (kC / 4)) * 4]) = na[i];
     }
@@ -502,63 +511,62 @@ __global__ __launch_bounds__(kScanThreads) void gdn_scan_kernel(GdnArgs p, const
     const float* knxt = kbase + (int64_t)cn * kWsPerKeyChunk;
     // ---- phase 1
     scan_load_kq(nxt, knxt, tid, nk, nq, neg);
-    // Y = diag(G) K S^T and O = diag(G) Q S^T on this wave's tile; inside
-    // each 16-wide K block the lane group lk takes k = 4 lk + s at step s
-    // (any order of k gives the same sum), so each operand is one 16-byte read
-    floatx4 accy = {0.0f, 0.0f, 0.0f, 0.0f}, acco = {0.0f, 0.0f, 0.0f, 0.0f};
+    // this wave's tile of Y = diag(G) K S^T or O = diag(G) Q S^T
+    floatx4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    {
+      const float(*src)[kP] = oprod ? sQ : sK;
 #pragma unroll
-    for (int kb = 0; kb < kD / 16; ++kb) {
-      const floatx4 bs = *reinterpret_cast<const floatx4*>(&sS[16 * tj + li][16 * kb + 4 * lk]);
-      const floatx4 ak = *reinterpret_cast<const floatx4*>(&sK[16 * ti + li][16 * kb + 4 * lk]);
-      const floatx4 aq = *reinterpret_cast<const floatx4*>(&sQ[16 * ti + li][16 * kb + 4 * lk]);
+      for (int kb = 0; kb < kD / 16; ++kb) {
+        const floatx4 bs = *reinterpret_cast<const floatx4*>(&sS[16 * tj + li][16 * kb + 4 * lk]);
+        const floatx4 as = *reinterpret_cast<const floatx4*>(&src[16 * ti + li][16 * kb + 4 * lk]);
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        accy = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[s2], bs[s2], accy, 0, 0, 0);
-        acco = __builtin_amdgcn_mfma_f32_16x16x4f32(aq[s2], bs[s2], acco, 0, 0, 0);
+        for (int s2 = 0; s2 < 4; ++s2) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(as[s2], bs[s2], acc1, 0, 0, 0);
       }
     }
-    *reinterpret_cast<floatx4*>(&sRT[16 * tj + li][16 * ti + 4 * lk]) =
-        floatx4{nb[0] * (nv[0] - accy[0]), nb[1] * (nv[1] - accy[1]), nb[2] * (nv[2] - accy[2]),
-                nb[3] * (nv[3] - accy[3])};
+    if (!oprod)
+      *reinterpret_cast<floatx4*>(&sRT[16 * tj + li][16 * ti + 4 * lk]) =
+          floatx4{nb[0] * (nv[0] - acc1[0]), nb[1] * (nv[1] - acc1[1]), nb[2] * (nv[2] - acc1[2]),
+                  nb[3] * (nv[3] - acc1[3])};
     put_za();
     __syncthreads();  // R, Z^T, A T of this chunk in LDS; every read of diag(G) K, diag(G) Q, S done
     // ---- phase 2
     const float gc = ngc;
     scan_load_za<DT>(nxt, p, tid, boff, (int64_t)cn * kC + boff, vcol, nz, na, nv, nb, ngc);
-    // O += (A T) R over key blocks kb <= ti (A T is lower triangular)
-    for (int kb = 0; kb <= ti; ++kb) {
-      const floatx4 aa = *reinterpret_cast<const floatx4*>(&sA[16 * ti + li][16 * kb + 4 * lk]);
-      const floatx4 br = *reinterpret_cast<const floatx4*>(&sRT[16 * tj + li][16 * kb + 4 * lk]);
+    if (oprod) {
+      // O += (A T) R over key blocks kb <= ti (A T is lower triangular)
+      for (int kb = 0; kb <= ti; ++kb) {
+        const floatx4 aa = *reinterpret_cast<const floatx4*>(&sA[16 * ti + li][16 * kb + 4 * lk]);
+        const floatx4 br = *reinterpret_cast<const floatx4*>(&sRT[16 * tj + li][16 * kb + 4 * lk]);
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) acco = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[s2], br[s2], acco, 0, 0, 0);
-    }
+        for (int s2 = 0; s2 < 4; ++s2) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[s2], br[s2], acc1, 0, 0, 0);
+      }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t tt = (int64_t)chunk * kC + 16 * ti + 4 * lk + q;
-      if (tt < p.T) {
-        const int64_t idx = tt * p.ld_o + (int64_t)h * kD + row0 + 16 * tj + li;
-        if constexpr (ODT == NVFP4_DTYPE_BF16)
-          reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)f32_to_bf16_bits(acco[q]);
-        else
-          reinterpret_cast<float*>(p.o)[idx] = acco[q];
+      for (int q = 0; q < 4; ++q) {
+        const int64_t tt = (int64_t)chunk * kC + 16 * ti + 4 * lk + q;
+        if (tt < p.T) {
+          const int64_t idx = tt * p.ld_o + (int64_t)h * kD + row0 + 16 * tj + li;
+          if constexpr (ODT == NVFP4_DTYPE_BF16)
+            reinterpret_cast<uint16_t*>(p.o)[idx] = (uint16_t)f32_to_bf16_bits(acc1[q]);
+          else
+            reinterpret_cast<float*>(p.o)[idx] = acc1[q];
+        }
       }
     }
-    // S[c][16w + j] = G_C S + R^T Z: each wave reads and writes only its own
-    // 16 columns of the slice
-#pragma unroll
-    for (int tc = 0; tc < 2; ++tc) {
+    // S[16 tc + i][16 cbk + j] = G_C S + R^T Z: each wave reads and writes
+    // only its own tile of the slice
+    {
       floatx4 acc;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = gc * sS[16 * tc + 4 * lk + q][16 * wave + li];
+      for (int q = 0; q < 4; ++q) acc[q] = gc * sS[16 * tc + 4 * lk + q][16 * cbk + li];
 #pragma unroll
       for (int kb = 0; kb < kC / 16; ++kb) {
         const floatx4 ar = *reinterpret_cast<const floatx4*>(&sRT[16 * tc + li][16 * kb + 4 * lk]);
-        const floatx4 bz = *reinterpret_cast<const floatx4*>(&sZT[16 * wave + li][16 * kb + 4 * lk]);
+        const floatx4 bz = *reinterpret_cast<const floatx4*>(&sZT[16 * cbk + li][16 * kb + 4 * lk]);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ar[s2], bz[s2], acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sS[16 * tc + 4 * lk + q][16 * wave + li] = acc[q];
+      for (int q = 0; q < 4; ++q) sS[16 * tc + 4 * lk + q][16 * cbk + li] = acc[q];
     }
     put_kq();         // the next chunk's diag(G) K, diag(G) Q
     __syncthreads();  // new S, next diag(G) K and Q in LDS; every read of this chunk's A T, Z^T, R done
