@@ -70,7 +70,7 @@ def check(o_gpu, s_gpu, q, k, v, beta, g, normalize=True, s0=None, out_bf16=Fals
     return worst
 
 
-@pytest.mark.parametrize("T,hk,hv", [(1, 1, 1), (63, 1, 2), (64, 2, 2), (200, 2, 6), (1000, 1, 3)])
+@pytest.mark.parametrize("T,hk,hv", [(1, 1, 1), (63, 1, 2), (64, 2, 2), (130, 1, 8), (200, 2, 6), (1000, 1, 3)])
 def test_gdn_matches_sequential_oracle(T, hk, hv):
     say(f"gdn {T}x{hk}/{hv}")
     rng = np.random.default_rng(T + hv)
